@@ -1,0 +1,226 @@
+"""fp64 CPU oracle for SQuad-Attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's smoke check and the benchmark's CPU-baseline leg
+may import this module.  The HIP library never calls it, and it shares no code
+with the HIP path (it does not import the package; inputs arrive as arrays).
+
+What is computed (SQuad: Sub-Quadratic Attention Distillation for Efficient
+Video Generation):
+
+* The operator composes two ordinary softmax attentions run one after the other,
+  with only re-indexing in between, where the axis not attended over is folded
+  into the head count (agihunt.info summary, method paragraph; paperpeel full
+  text, sec. 3.2 and appendix E "Cost of the two passes").
+* Local pass: tokens mix within fixed windows of about sqrt(n) tokens, cut from
+  the latent grid and spanning the whole temporal extent (agihunt.info summary;
+  paperpeel full text, sec. 1, last paragraph).
+* Global pass: tokens at the same position inside each window mix across all
+  windows (paperpeel full text, sec. 1; appendix "Reachability").  The local
+  output feeds the value stream of the global pass (gist.science explainer,
+  "Operador de Atencao SQuad").  Since nothing but re-indexing sits between the
+  passes and no parameters are added, the global pass takes the same Q and K
+  re-indexed.
+* Each attention is the plain softmax(Q K^T / sqrt(d)) V (paperpeel full text,
+  sec. 1), non-causal, every query attending to its own key too.
+
+Readings where the pages are silent (listed again in the design notes):
+  token order inside the grid is (t, y, x) row-major; windows are aligned,
+  non-overlapping tiles anchored at the origin; the slot of a token is its
+  in-window offset (t % wt, y % wh, x % ww); the scale is 1/sqrt(d) in both
+  passes.
+
+Every function is pinned by tests/test_oracle.py against closed forms, library
+attention, brute force over token pairs and the FLOP counts the pages print.
+"""
+
+from __future__ import annotations
+
+import math
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Re-indexing: window c and slot j of every token
+# ---------------------------------------------------------------------------
+
+def window_slot_table(T, Hs, Ws, wt, wh, ww):
+    """Token index of (window c, slot j) as an int64 array of shape [N_w, m].
+
+    Windows are the aligned (wt, wh, ww) tiles of the (T, Hs, Ws) grid, numbered
+    in (t, y, x) row-major order of their tile coordinates; the slot is the
+    token's offset inside its window, numbered the same way.  Token (t, y, x)
+    has index (t * Hs + y) * Ws + x.
+    """
+    if T % wt or Hs % wh or Ws % ww:
+        raise ValueError("window must tile the grid")
+    Ct, Cy, Cx = T // wt, Hs // wh, Ws // ww
+    table = np.empty((Ct * Cy * Cx, wt * wh * ww), dtype=np.int64)
+    for ct in range(Ct):
+        for cy in range(Cy):
+            for cx in range(Cx):
+                c = (ct * Cy + cy) * Cx + cx
+                for jt in range(wt):
+                    for jy in range(wh):
+                        for jx in range(ww):
+                            j = (jt * wh + jy) * ww + jx
+                            t, y, x = ct * wt + jt, cy * wh + jy, cx * ww + jx
+                            table[c, j] = (t * Hs + y) * Ws + x
+    return table
+
+
+# ---------------------------------------------------------------------------
+# One ordinary softmax attention
+# ---------------------------------------------------------------------------
+
+def softmax_attention(q, k, v):
+    """softmax(q k^T / sqrt(d)) v over the last two axes, in float64.
+
+    q, k: [..., L, d]; v: [..., L, dv].  The row maximum is subtracted before
+    exponentiating, which leaves the softmax unchanged.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(q.shape[-1])
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return np.matmul(p, v)
+
+
+# ---------------------------------------------------------------------------
+# The two passes on one (batch, head) slice: arrays [n, d]
+# ---------------------------------------------------------------------------
+
+def local_pass_head(q, k, v, table):
+    """Attn_L: every window attends within itself.  q, k, v: [n, d] -> [n, d]."""
+    out = np.empty(np.shape(v), dtype=np.float64)
+    # gather [N_w, m, d]: the attended axis (slots) becomes the sequence, the
+    # window axis is folded into the batch/head count
+    out[table] = softmax_attention(q[table], k[table], v[table])
+    return out
+
+
+def global_pass_head(q, k, v, table):
+    """Attn_G: tokens sharing a slot attend across all windows.  [n, d] -> [n, d]."""
+    cols = table.T  # [m, N_w]: the attended axis (windows) becomes the sequence
+    out = np.empty(np.shape(v), dtype=np.float64)
+    out[cols] = softmax_attention(q[cols], k[cols], v[cols])
+    return out
+
+
+def squad_head(q, k, v, table):
+    """Local pass, then global pass with the same q, k and the local output as values."""
+    y = local_pass_head(q, k, v, table)
+    return global_pass_head(q, k, y, table)
+
+
+def squad_reversed_head(q, k, v, table):
+    """The other order (global first, then local), as in the ordering ablation."""
+    y = global_pass_head(q, k, v, table)
+    return local_pass_head(q, k, y, table)
+
+
+# ---------------------------------------------------------------------------
+# Whole tensors in [B, n, heads, d] layout
+# ---------------------------------------------------------------------------
+
+def _per_head(fn, q, k, v, geom):
+    B, heads, T, Hs, Ws, wt, wh, ww, d = geom
+    table = window_slot_table(T, Hs, Ws, wt, wh, ww)
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(q.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(heads):
+            out[b, :, h, :] = fn(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :], table)
+    return out
+
+
+def squad_attention(q, k, v, geom):
+    """O = Attn_G(Q, K, Attn_L(Q, K, V)) for [B, n, heads, d] inputs; geom =
+    (B, heads, T, Hs, Ws, wt, wh, ww, d)."""
+    return _per_head(squad_head, q, k, v, geom)
+
+
+def local_pass(q, k, v, geom):
+    return _per_head(local_pass_head, q, k, v, geom)
+
+
+def global_pass(q, k, v, geom):
+    return _per_head(global_pass_head, q, k, v, geom)
+
+
+def squad_attention_reversed(q, k, v, geom):
+    return _per_head(squad_reversed_head, q, k, v, geom)
+
+
+# ---------------------------------------------------------------------------
+# Dense n x n form (tiny n only): masks and the effective weight matrix
+# ---------------------------------------------------------------------------
+
+def token_coords(T, Hs, Ws):
+    """(t, y, x) of every token index, [n, 3]."""
+    t, y, x = np.meshgrid(np.arange(T), np.arange(Hs), np.arange(Ws), indexing="ij")
+    return np.stack([t.ravel(), y.ravel(), x.ravel()], axis=1)
+
+
+def dense_masks(T, Hs, Ws, wt, wh, ww):
+    """Boolean [n, n] masks: same window (local pass) and same slot (global pass).
+
+    Built from grid coordinates alone (no window/slot table), as an independent
+    formulation of the two index sets.
+    """
+    c = token_coords(T, Hs, Ws)
+    w = np.array([wt, wh, ww])
+    win = c // w
+    slot = c % w
+    same_window = np.all(win[:, None, :] == win[None, :, :], axis=-1)
+    same_slot = np.all(slot[:, None, :] == slot[None, :, :], axis=-1)
+    return same_window, same_slot
+
+
+def masked_softmax_weights(q, k, mask):
+    """Row-stochastic [n, n] matrix softmax over the allowed keys of q k^T / sqrt(d)."""
+    s = (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T) / math.sqrt(q.shape[-1])
+    s = np.where(mask, s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.where(mask, np.exp(s), 0.0)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def effective_weights(q, k, T, Hs, Ws, wt, wh, ww):
+    """(A_L, A_G, W) for one head: the local weights (beta), the global weights
+    (alpha) and the effective weight W = A_G A_L, whose entry for target (c, j)
+    and source (c', j') is alpha^j_{c->c'} beta^{c'}_{j->j'} (paperpeel full
+    text, appendix "Unrolling the composition" / "Reachability")."""
+    same_window, same_slot = dense_masks(T, Hs, Ws, wt, wh, ww)
+    a_local = masked_softmax_weights(q, k, same_window)
+    a_global = masked_softmax_weights(q, k, same_slot)
+    return a_local, a_global, a_global @ a_local
+
+
+# ---------------------------------------------------------------------------
+# FLOP count of the two passes
+# ---------------------------------------------------------------------------
+
+def squad_flops(B, heads, T, Hs, Ws, wt, wh, ww, d):
+    """FLOPs of the operator counting 2 per multiply-add in the two matmuls of
+    each softmax attention (scores and weighted sum), nothing else.
+
+    The local pass runs B*heads*N_w attentions of length m, the global pass
+    B*heads*m attentions of length N_w; one attention of length L costs
+    2 * (L*L*d) * 2 FLOPs.
+    """
+    n = T * Hs * Ws
+    m = wt * wh * ww
+    n_w = n // m
+    local = B * heads * n_w * (2 * 2 * m * m * d)
+    glob = B * heads * m * (2 * 2 * n_w * n_w * d)
+    return local + glob
+
+
+def full_attention_flops(B, heads, n, d):
+    """FLOPs of one full softmax attention over n tokens, same counting rule."""
+    return B * heads * 2 * 2 * n * n * d

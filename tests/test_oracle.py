@@ -1,0 +1,367 @@
+"""Pins for the fp64 oracle (CPU only).
+
+The oracle is only trusted once it agrees with things fixed independently of it:
+library softmax attention in the special cases where SQuad reduces to it, a
+pure-Python brute force over token pairs, closed forms, invariants of softmax,
+and the FLOP counts printed on the pages.  The last test plants plausible
+mistakes in copies of the oracle and checks that these pins catch every one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import squad_oracle as so
+from sub_quadratic_factorized_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand(shape, seed, scale=1.0):
+    g = np.random.Generator(np.random.PCG64(seed))
+    return g.standard_normal(shape) * scale
+
+
+def sdpa_f64(q, k, v):
+    """Library softmax attention (torch CPU, float64), 1/sqrt(d) scale, no mask."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0].numpy()
+
+
+# ---------------------------------------------------------------------------
+# Pure-Python brute force (no numpy arithmetic): token pairs from coordinates
+# ---------------------------------------------------------------------------
+
+def brute_force_head(q, k, v, T, Hs, Ws, wt, wh, ww):
+    """O = W V with W[i][i'] = sum_i'' alpha[i][i''] beta[i''][i'] built by loops."""
+    n, d = len(q), len(q[0])
+    coords = [(t, y, x) for t in range(T) for y in range(Hs) for x in range(Ws)]
+    same_win = lambda a, b: all(coords[a][e] // w == coords[b][e] // w for e, w in enumerate((wt, wh, ww)))
+    same_slot = lambda a, b: all(coords[a][e] % w == coords[b][e] % w for e, w in enumerate((wt, wh, ww)))
+
+    def weights(pred):
+        rows = []
+        for i in range(n):
+            keys = [j for j in range(n) if pred(i, j)]
+            s = {j: sum(q[i][e] * k[j][e] for e in range(d)) / math.sqrt(d) for j in keys}
+            mx = max(s.values())
+            ex = {j: math.exp(s[j] - mx) for j in keys}
+            tot = sum(ex.values())
+            rows.append([ex.get(j, 0.0) / tot for j in range(n)])
+        return rows
+
+    beta = weights(same_win)   # local weights
+    alpha = weights(same_slot)  # global weights
+    W = [[sum(alpha[i][l] * beta[l][j] for l in range(n)) for j in range(n)] for i in range(n)]
+    O = [[sum(W[i][j] * v[j][e] for j in range(n)) for e in range(len(v[0]))] for i in range(n)]
+    return np.array(W), np.array(O)
+
+
+TINY = (3, 4, 4, 3, 2, 2)           # the tiny workload's grid and window
+ODD = (2, 3, 4, 1, 3, 2)            # a second geometry: 6 windows of 6 tokens
+
+
+# ---------------------------------------------------------------------------
+# Checks, parametrised by the per-head implementation so mutants can be fed in
+# ---------------------------------------------------------------------------
+
+def check_brute_force(impl, geo=TINY, d=8, seed=1):
+    T, Hs, Ws, wt, wh, ww = geo
+    n = T * Hs * Ws
+    q, k, v = rand((n, d), seed), rand((n, d), seed + 1), rand((n, d), seed + 2)
+    _, O_ref = brute_force_head(q.tolist(), k.tolist(), v.tolist(), *geo)
+    O = impl(q, k, v, so.window_slot_table(*geo))
+    return np.max(np.abs(O - O_ref)) < 1e-12
+
+
+def check_single_window(impl, seed=3):
+    # one window spanning the grid: SQuad == full attention (global pass over one window is identity)
+    T, Hs, Ws, d = 3, 4, 5, 16
+    n = T * Hs * Ws
+    q, k, v = rand((n, d), seed), rand((n, d), seed + 1), rand((n, d), seed + 2)
+    O = impl(q, k, v, so.window_slot_table(T, Hs, Ws, T, Hs, Ws))
+    return np.max(np.abs(O - sdpa_f64(q, k, v))) < 1e-12
+
+
+def check_single_token_windows(impl, seed=4):
+    # 1x1x1 windows: local pass is identity, global pass is full attention
+    T, Hs, Ws, d = 2, 3, 5, 16
+    n = T * Hs * Ws
+    q, k, v = rand((n, d), seed), rand((n, d), seed + 1), rand((n, d), seed + 2)
+    O = impl(q, k, v, so.window_slot_table(T, Hs, Ws, 1, 1, 1))
+    return np.max(np.abs(O - sdpa_f64(q, k, v))) < 1e-12
+
+
+def check_zero_query(impl, geo=ODD, seed=5):
+    # Q = 0: both softmaxes are uniform, so every token receives the mean of V
+    T, Hs, Ws, wt, wh, ww = geo
+    n, d = T * Hs * Ws, 8
+    k, v = rand((n, d), seed), rand((n, d), seed + 1)
+    O = impl(np.zeros((n, d)), k, v, so.window_slot_table(*geo))
+    return np.max(np.abs(O - v.mean(axis=0))) < 1e-12
+
+
+ALL_CHECKS = [check_brute_force, check_single_window, check_single_token_windows, check_zero_query,
+              lambda impl: check_brute_force(impl, geo=ODD, d=5, seed=11)]
+
+
+# ---------------------------------------------------------------------------
+# Pins on the oracle itself
+# ---------------------------------------------------------------------------
+
+def test_window_slot_table_is_the_tiling():
+    for geo in (TINY, ODD, (21, 22, 40, 21, 2, 4)):
+        T, Hs, Ws, wt, wh, ww = geo
+        tab = so.window_slot_table(*geo)
+        assert tab.shape == ((T // wt) * (Hs // wh) * (Ws // ww), wt * wh * ww)
+        assert np.array_equal(np.sort(tab.ravel()), np.arange(T * Hs * Ws))  # a bijection
+        coords = so.token_coords(T, Hs, Ws)[tab]          # [N_w, m, 3]
+        w = np.array([wt, wh, ww])
+        win, slot = coords // w, coords % w
+        assert np.all(win == win[:, :1, :])                # a row is one window
+        assert np.all(slot == slot[:1, :, :])              # a column is one slot
+    # 5B native point: 110 windows of 168 tokens (agihunt.info summary, method paragraph)
+    assert so.window_slot_table(21, 22, 40, 21, 2, 4).shape == (110, 168)
+
+
+def test_token_index_is_row_major():
+    tab = so.window_slot_table(2, 2, 2, 1, 1, 1)
+    assert tab.ravel().tolist() == list(range(8))
+
+
+def test_brute_force_pin():
+    assert check_brute_force(so.squad_head)
+    assert check_brute_force(so.squad_head, geo=ODD, d=5, seed=11)
+
+
+def test_brute_force_pin_tiny_workload_shape():
+    # the tiny workload's own shape and head dim, one head
+    w = wl.WORKLOADS["tiny_f32"]
+    q, k, v = wl.head_slices_f64(w, 0, 1)
+    _, O_ref = brute_force_head(q.tolist(), k.tolist(), v.tolist(), w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
+    O = so.squad_head(q, k, v, so.window_slot_table(w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww))
+    assert np.max(np.abs(O - O_ref)) < 1e-12
+
+
+def test_single_window_is_full_attention():
+    assert check_single_window(so.squad_head)
+    T, Hs, Ws, d = 3, 4, 5, 16
+    n = T * Hs * Ws
+    q, k, v = rand((n, d), 7), rand((n, d), 8), rand((n, d), 9)
+    tab = so.window_slot_table(T, Hs, Ws, T, Hs, Ws)
+    assert np.max(np.abs(so.local_pass_head(q, k, v, tab) - sdpa_f64(q, k, v))) < 1e-12
+    assert np.array_equal(so.global_pass_head(q, k, v, tab), v)  # N_w = 1: identity
+
+
+def test_single_token_windows():
+    assert check_single_token_windows(so.squad_head)
+    T, Hs, Ws, d = 2, 3, 5, 16
+    n = T * Hs * Ws
+    q, k, v = rand((n, d), 7), rand((n, d), 8), rand((n, d), 9)
+    tab = so.window_slot_table(T, Hs, Ws, 1, 1, 1)
+    assert np.array_equal(so.local_pass_head(q, k, v, tab), v)  # m = 1: identity
+    assert np.max(np.abs(so.global_pass_head(q, k, v, tab) - sdpa_f64(q, k, v))) < 1e-12
+
+
+def test_zero_query_gives_global_mean():
+    assert check_zero_query(so.squad_head)
+
+
+def test_each_pass_against_library_attention_per_index_set():
+    # each local problem is library attention over the window's rows; each global one over the slot's rows
+    T, Hs, Ws, wt, wh, ww = ODD
+    n, d = T * Hs * Ws, 12
+    q, k, v = rand((n, d), 21), rand((n, d), 22), rand((n, d), 23)
+    tab = so.window_slot_table(*ODD)
+    y = so.local_pass_head(q, k, v, tab)
+    o = so.global_pass_head(q, k, y, tab)
+    for c in range(tab.shape[0]):
+        r = tab[c]
+        assert np.max(np.abs(y[r] - sdpa_f64(q[r], k[r], v[r]))) < 1e-12
+    for j in range(tab.shape[1]):
+        r = tab[:, j]
+        assert np.max(np.abs(o[r] - sdpa_f64(q[r], k[r], y[r]))) < 1e-12
+
+
+def test_dense_masked_form_matches_reindexed_form():
+    for geo, d in ((TINY, 64), (ODD, 7)):
+        T, Hs, Ws, wt, wh, ww = geo
+        n = T * Hs * Ws
+        q, k, v = rand((n, d), 31), rand((n, d), 32), rand((n, d), 33)
+        a_l, a_g, W = so.effective_weights(q, k, *geo)
+        O = so.squad_head(q, k, v, so.window_slot_table(*geo))
+        assert np.max(np.abs(W @ v - O)) < 1e-12
+        assert np.max(np.abs(a_g @ (a_l @ v) - O)) < 1e-12
+
+
+def test_effective_weight_positive_and_stochastic():
+    # no structural zeros; a product of two row-stochastic matrices is row-stochastic
+    for geo in (TINY, ODD):
+        T, Hs, Ws, wt, wh, ww = geo
+        n, d = T * Hs * Ws, 16
+        q, k = rand((n, d), 41, 2.0), rand((n, d), 42, 2.0)
+        a_l, a_g, W = so.effective_weights(q, k, *geo)
+        assert np.all(W > 0)
+        assert np.max(np.abs(W.sum(axis=1) - 1)) < 1e-12
+        # the factors themselves do have zeros (each pass alone has a restricted field)
+        assert np.any(a_l == 0) and np.any(a_g == 0)
+
+
+def test_reachability_two_hops():
+    # source (c', j') reaches target (c, j) through (c', j): beta^{c'}_{j->j'} > 0 and alpha^{j}_{c->c'} > 0
+    T, Hs, Ws, wt, wh, ww = TINY
+    n, d = T * Hs * Ws, 8
+    q, k = rand((n, d), 51), rand((n, d), 52)
+    a_l, a_g, W = so.effective_weights(q, k, *TINY)
+    tab = so.window_slot_table(*TINY)
+    for c in range(tab.shape[0]):
+        for j in range(tab.shape[1]):
+            for c2 in range(tab.shape[0]):
+                for j2 in range(tab.shape[1]):
+                    tgt, src, mid = tab[c, j], tab[c2, j2], tab[c2, j]
+                    via = a_g[tgt, mid] * a_l[mid, src]
+                    assert via > 0
+                    assert abs(W[tgt, src] - via) < 1e-15  # the only path in L->G order
+
+
+def test_constant_and_affine_values():
+    T, Hs, Ws, wt, wh, ww = TINY
+    n, d = T * Hs * Ws, 16
+    q, k, v = rand((n, d), 61), rand((n, d), 62), rand((n, d), 63)
+    tab = so.window_slot_table(*TINY)
+    const = np.tile(rand((1, d), 64), (n, 1))
+    assert np.max(np.abs(so.squad_head(q, k, const, tab) - const)) < 1e-12
+    a, b = -1.7, rand((1, d), 65)
+    O = so.squad_head(q, k, v, tab)
+    assert np.max(np.abs(so.squad_head(q, k, a * v + b, tab) - (a * O + b))) < 1e-12
+
+
+def test_key_shift_invariance():
+    T, Hs, Ws, wt, wh, ww = TINY
+    n, d = T * Hs * Ws, 16
+    q, k, v = rand((n, d), 71), rand((n, d), 72), rand((n, d), 73)
+    tab = so.window_slot_table(*TINY)
+    u = rand((1, d), 74)
+    assert np.max(np.abs(so.squad_head(q, k + u, v, tab) - so.squad_head(q, k, v, tab))) < 1e-12
+
+
+def test_orders_differ_but_both_dense():
+    T, Hs, Ws, wt, wh, ww = TINY
+    n, d = T * Hs * Ws, 16
+    q, k, v = rand((n, d), 81), rand((n, d), 82), rand((n, d), 83)
+    tab = so.window_slot_table(*TINY)
+    lg = so.squad_head(q, k, v, tab)
+    gl = so.squad_reversed_head(q, k, v, tab)
+    assert np.max(np.abs(lg - gl)) > 1e-3
+    a_l, a_g, _ = so.effective_weights(q, k, *TINY)
+    W_gl = a_l @ a_g
+    assert np.all(W_gl > 0)
+    assert np.max(np.abs(W_gl @ v - gl)) < 1e-12
+
+
+def test_flop_count_matches_printed_numbers():
+    with open(os.path.join(GOLDEN, "printed_flops.json")) as f:
+        gold = json.load(f)
+    tol = gold["full_attention_rel_tolerance"]
+    for e in gold["entries"]:
+        T, Hs, Ws = e["grid"]
+        wt, wh, ww = e["window"]
+        assert T * Hs * Ws == e["n"]
+        f = so.squad_flops(1, e["heads"], T, Hs, Ws, wt, wh, ww, e["d"])
+        digits = len(str(e["squad_tflops"]).split(".")[1])
+        assert round(f / 1e12, digits) == e["squad_tflops"], e["backbone"]
+        full = so.full_attention_flops(1, e["heads"], e["n"], e["d"])
+        assert abs(full / 1e12 - e["full_tflops"]) / e["full_tflops"] <= tol, e["backbone"]
+        assert round(full / f) == round(e["ratio"]) or abs(full / f - e["ratio"]) < 0.5
+        # closed form 4 h d n (m + n/m) (paperpeel full text, appendix, FLOP conformance paragraph)
+        m = wt * wh * ww
+        assert f == 4 * e["heads"] * e["d"] * e["n"] * (m + e["n"] // m)
+
+
+def test_flop_count_closed_form_everywhere():
+    for w in wl.WORKLOADS.values():
+        f = so.squad_flops(*w.geometry())
+        assert f == 4 * w.B * w.heads * w.d * w.n * (w.m + w.n_windows)
+    assert so.squad_flops(1, 24, 21, 22, 40, 21, 2, 4, 128) == 63_128_862_720
+
+
+def test_oracle_on_tiny_workload_prescaled_variant_is_consistent():
+    # the literal "scaled by 1/sqrt(d)" reading of the tiny workload: same operator, smaller logits
+    w = wl.WORKLOADS["tiny_f32_prescaled"]
+    q, k, v = wl.full_inputs_f32(w)
+    O = so.squad_attention(q, k, v, w.geometry())
+    for h in range(w.heads):
+        _, _, W = so.effective_weights(q[0, :, h].astype(np.float64), k[0, :, h].astype(np.float64),
+                                       w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
+        assert np.max(np.abs(W @ v[0, :, h] - O[0, :, h])) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each mutant of the oracle must fail at least one pin
+# ---------------------------------------------------------------------------
+
+def _mut_values_not_composed(q, k, v, tab):
+    so.local_pass_head(q, k, v, tab)
+    return so.global_pass_head(q, k, v, tab)
+
+
+def _mut_no_scale(q, k, v, tab):
+    return so.squad_head(q * math.sqrt(q.shape[1]), k, v, tab)
+
+
+def _mut_swapped_index_sets(q, k, v, tab):
+    return so.squad_head(q, k, v, np.ascontiguousarray(tab.T))
+
+
+def _mut_reversed_order(q, k, v, tab):
+    return so.squad_reversed_head(q, k, v, tab)
+
+
+def _mut_global_keys_are_queries(q, k, v, tab):
+    y = so.local_pass_head(q, k, v, tab)
+    return so.global_pass_head(q, q, y, tab)
+
+
+def _mut_negated_scores(q, k, v, tab):
+    return so.squad_head(-q, k, v, tab)
+
+
+def _mut_transposed_scores(q, k, v, tab):
+    # scores k q^T instead of q k^T in the local pass
+    y = np.empty_like(v)
+    for c in range(tab.shape[0]):
+        r = tab[c]
+        s = (k[r] @ q[r].T) / math.sqrt(q.shape[1])
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        y[r] = (p / p.sum(axis=1, keepdims=True)) @ v[r]
+    return so.global_pass_head(q, k, y, tab)
+
+
+def _mut_local_only(q, k, v, tab):
+    return so.local_pass_head(q, k, v, tab)
+
+
+def _mut_no_self_key(q, k, v, tab):
+    # excludes each query's own key in the local pass
+    y = np.empty_like(v)
+    for c in range(tab.shape[0]):
+        r = tab[c]
+        s = (q[r] @ k[r].T) / math.sqrt(q.shape[1])
+        np.fill_diagonal(s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        y[r] = (p / p.sum(axis=1, keepdims=True)) @ v[r]
+    return so.global_pass_head(q, k, y, tab)
+
+
+@pytest.mark.parametrize("mutant", [
+    _mut_values_not_composed, _mut_no_scale, _mut_swapped_index_sets, _mut_reversed_order,
+    _mut_global_keys_are_queries, _mut_negated_scores, _mut_transposed_scores, _mut_local_only,
+    _mut_no_self_key,
+])
+def test_pins_catch_planted_mistakes(mutant):
+    assert all(chk(so.squad_head) for chk in ALL_CHECKS)
+    assert not all(chk(mutant) for chk in ALL_CHECKS), mutant.__name__
