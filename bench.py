@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the SQuad-Attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 150] [--warmup 5]
+
+One step is one squad_attn_fwd call (local pass, then global pass) over the
+Wan 2.2 5B-shaped block at 704x1280x81: n = 18,480 tokens (grid 21x22x40),
+24 heads of dim 128, window 21x2x4 (168 tokens, 110 windows), bf16.  Inputs are
+seeded synthetic tensors of that shape already resident in HBM; two complete
+input/output sets are used alternately so that the 256 MB last-level cache
+cannot hold a whole set between steps.
+
+Prints one JSON line: effective TFLOP/s (algorithmic FLOPs 4*B*h*d*n*(m+N_w)
+per step over the measured time) plus ms per block, a roofline object for the
+dominant kernel (its own launches timed with HIP events on the launch stream)
+and the oracle's throughput on the host cores (a bounded sample).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PAGES_MS_PER_BLOCK = 4.27      # the pages' SQuad attention latency per block (H100, bf16, n = 18,480)
+KERNEL_SOURCES = ["sub_quadratic_factorized_amd/csrc/squad_pass_bf16.hip",
+                  "sub_quadratic_factorized_amd/csrc/squad_internal.h"]
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def time_loop(fn, iters, sets, warmup=2):
+    """Average ms per call of fn(set) over `iters` calls, HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(iters):
+        fn(sets[i % len(sets)])
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The fp64 oracle on host cores over a bounded sample of the workload's heads."""
+    import numpy as np
+    from oracle import squad_oracle as so
+    from sub_quadratic_factorized_amd import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = 1
+    table = so.window_slot_table(w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
+    heads_done, elapsed = 0, 0.0
+    per_head_flops = so.squad_flops(1, 1, w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww, w.d)
+    q, k, v = wl.head_slices_f64(w, 0, 0)
+    so.squad_head(q, k, v, table)  # warm-up, untimed
+    for h in range(w.heads):
+        q, k, v = wl.head_slices_f64(w, 0, h)
+        t0 = time.perf_counter()
+        so.squad_head(q, k, v, table)
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+        if elapsed > budget_s:
+            break
+    rate = heads_done * per_head_flops / elapsed / 1e12
+    return {
+        "value": rate,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{heads_done} of {w.heads} heads (b=0) of {w.name}, numpy float64, "
+                  f"{elapsed:.2f} s; scaled per head ({w.name} has {w.B * w.heads} (b, head) slices)",
+        "ms_per_block_equiv": elapsed / heads_done * w.B * w.heads * 1e3,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=150)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 5B 704p block)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=100)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sub_quadratic_factorized_amd import binding as bd
+    from sub_quadratic_factorized_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    bd.lib()  # fail loudly if the HIP library is missing
+
+    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
+    grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)
+    flops = bd.squad_attn_flops(*w.geometry())
+    dt = bd.SQUAD_BF16 if w.dtype == "bf16" else bd.SQUAD_F32
+    bytes_fwd = bd.squad_attn_bytes(*w.geometry(), dt)
+    pass_bytes = bytes_fwd / 2  # each pass reads three tensors and writes one
+
+    eprint(f"[bench] workload {w.name}: generating inputs")
+    q, k, v = wl.device_inputs(w, seed=0)
+    sets = [(q, k, v, torch.empty_like(q))]
+    # a second, different set (rotated inputs keep the last-level cache honest)
+    sets.append((q.roll(1, dims=2).contiguous(), k.roll(1, dims=2).contiguous(), v.roll(1, dims=2).contiguous(),
+                 torch.empty_like(q)))
+    torch.cuda.synchronize()
+
+    def step(s):
+        bd.squad_attn_fwd(s[0], s[1], s[2], grid, window, out=s[3])
+
+    # ---- the timed region: exactly `steps` forward passes --------------------
+    for i in range(args.warmup):
+        step(sets[i % 2])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(sets[i % 2])
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(per) / len(per)
+    ms_per_step = wall * 1e3 / args.steps
+    eprint(f"[bench] fwd: wall {ms_per_step:.4f} ms/step, event mean {mean_ms:.4f} median {per[len(per)//2]:.4f} "
+           f"min {per[0]:.4f} ms")
+
+    # warm (single set) figure for reference
+    warm_ms = time_loop(step, args.kernel_iters, sets[:1])
+
+    # ---- per-kernel timing for the roofline ---------------------------------
+    def local(s):
+        bd.squad_attn_local(s[0], s[1], s[2], grid, window, out=s[3])
+
+    def glob(s):
+        bd.squad_attn_global(s[0], s[1], s[3], grid, window, out=s[3])
+
+    local_ms = time_loop(local, args.kernel_iters, sets)
+    global_ms = time_loop(glob, args.kernel_iters, sets)
+    eprint(f"[bench] local pass {local_ms:.4f} ms/launch, global pass {global_ms:.4f} ms/launch, warm fwd {warm_ms:.4f}")
+    dom, dom_ms = ("local", local_ms) if local_ms >= global_ms else ("global", global_ms)
+    kname = "squad_local_pass" if dom == "local" else "squad_global_pass"
+    achieved = pass_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(kname, w.name)
+
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": "SQuad attn ms/block + effective TFLOP/s & % roofline, n=18480 h=24 d=128 bf16",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": PAGES_MS_PER_BLOCK / ms_per_step if w.name == wl.HEADLINE else None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "heads": w.heads, "d": w.d, "grid": list(grid), "window": list(window),
+            "n": w.n, "m": w.m, "n_windows": w.n_windows, "input_sets_rotated": 2,
+        },
+        "ms_per_block": {"wall_mean": ms_per_step, "event_mean": mean_ms, "event_median": per[len(per) // 2],
+                         "event_min": per[0], "warm_single_set": warm_ms},
+        "effective_tflops": value,
+        "algorithmic_gbs": bytes_fwd / (ms_per_step * 1e-3) / 1e9,
+        "fraction_of_roofline": (bytes_fwd / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
+        "kernels_ms": {"squad_local_pass": local_ms, "squad_global_pass": global_ms},
+        "roofline": {
+            "kernel": kname,
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": pass_bytes,
+            "mfma_tflops": (flops * (w.m if dom == "local" else w.n_windows) / (w.m + w.n_windows))
+                           / (dom_ms * 1e-3) / 1e12,
+            "mfma_peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+        },
+        "baseline_context": {"pages_ms_per_block": PAGES_MS_PER_BLOCK, "hardware": "NVIDIA H100 80GB (pages)"},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        eprint("[bench] timing the oracle on host cores (bounded sample)")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

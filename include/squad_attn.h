@@ -1,0 +1,146 @@
+/*
+ * squad_attn.h -- C ABI of the SQuad-Attention forward pass on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operator (SQuad: Sub-Quadratic Attention Distillation for Efficient
+ * Video Generation) replaces one full softmax self-attention over the n latent
+ * tokens of a video DiT block by two ordinary softmax attentions composed
+ * (agihunt.info summary, method paragraph; paperpeel full text, sec. 3.2):
+ *
+ *   local pass   Y[c,j] = sum_{j'} softmax_{j'}(<Q[c,j], K[c,j']> / sqrt(d)) V[c,j']
+ *                over the m = wt*wh*ww tokens of window c (every window spans
+ *                the full temporal extent in the pages' configuration);
+ *   global pass  O[c,j] = sum_{c'} softmax_{c'}(<Q[c,j], K[c',j]> / sqrt(d)) Y[c',j]
+ *                over the N_w = n/m windows, at the fixed in-window slot j
+ *                (paperpeel full text, appendix "Reachability"),
+ *
+ * where [c,j] is the token at slot j of window c, the global pass reuses the
+ * block's Q and K (only re-indexing sits between the passes and the method adds
+ * no parameters) and the local output is its value stream (gist.science
+ * explainer, "Operador de Atencao SQuad").  Both softmaxes are non-causal and
+ * include the query's own key.
+ *
+ * Layout.  q, k, v and out are contiguous device buffers [B, n, heads, d] of
+ * one dtype, n = T*Hs*Ws tokens in (t, y, x) row-major order: element
+ * (b, i, h, e) sits at ((b*n + i)*heads + h)*d + e.  Windows are the aligned
+ * (wt, wh, ww) tiles of the (T, Hs, Ws) grid, numbered in row-major order of
+ * their tile coordinates; the slot of a token is its in-window offset
+ * (t%wt, y%wh, x%ww), numbered row-major.
+ *
+ * Ownership.  The caller allocates and owns every buffer.  The library keeps no
+ * per-call state and allocates nothing; out doubles as the intermediate Y of
+ * squad_attn_fwd, so no workspace is needed.  Prior contents of out are
+ * ignored; they are undefined after a failed launch.
+ *
+ * Semantics.  Every compute entry point is asynchronous on `stream` (0 = the
+ * null stream): it validates its arguments on the host, before any HIP call,
+ * enqueues its kernels and returns.  Device faults surface at the caller's
+ * next synchronisation.  out may be the very same buffer as v (the update is
+ * then in place); any other overlap of out with q, k or v is rejected.
+ * B == 0 or heads == 0 is an empty problem: SQUAD_OK, nothing is enqueued and
+ * the pointers are not inspected.
+ *
+ * Errors (checked in this order; the first failing check is returned):
+ *   SQUAD_ERR_SHAPE       a negative B or heads; any other dimension < 1;
+ *                         T % wt, Hs % wh or Ws % ww != 0; the element count
+ *                         B*n*heads*d overflowing 62 bits; B*heads*max(m, N_w)
+ *                         not fitting a 31-bit launch grid.
+ *   SQUAD_ERR_UNSUPPORTED unknown dtype; d not in {64, 128}; m or N_w above
+ *                         squad_attn_max_len(d, dtype).
+ *   SQUAD_ERR_NULL        q, k, v or out is NULL.
+ *   SQUAD_ERR_ALIGN       a pointer not 16-byte aligned.
+ *   SQUAD_ERR_ALIAS       out overlaps q or k, or overlaps v without being v.
+ *   SQUAD_ERR_HIP         a HIP runtime call or kernel launch failed
+ *                         (squad_attn_last_hip_error() gives the hipError_t).
+ */
+#ifndef SQUAD_ATTN_H
+#define SQUAD_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQUAD_BF16 = 0, /* bfloat16 storage, bf16 MFMA with fp32 accumulation */
+    SQUAD_F32 = 1   /* float32 storage and arithmetic (debug / reference path) */
+} squad_dtype_t;
+
+typedef enum {
+    SQUAD_OK = 0,
+    SQUAD_ERR_NULL = 1,
+    SQUAD_ERR_SHAPE = 2,
+    SQUAD_ERR_UNSUPPORTED = 3,
+    SQUAD_ERR_ALIAS = 4,
+    SQUAD_ERR_ALIGN = 5,
+    SQUAD_ERR_HIP = 6
+} squad_status_t;
+
+/* out = Attn_G(q, k, Attn_L(q, k, v)): the SQuad-Attention forward pass.
+ * Enqueues the local pass (writing Y into out) and then the global pass
+ * (reading Y from out and writing O over it, each workgroup reading its whole
+ * read set before it writes the same rows). */
+squad_status_t squad_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                              int B, int heads, int T, int Hs, int Ws,
+                              int wt, int wh, int ww, int d,
+                              int dtype, hipStream_t stream);
+
+/* out = Attn_L(q, k, v): the local (in-window) pass alone. */
+squad_status_t squad_attn_local(const void* q, const void* k, const void* v, void* out,
+                                int B, int heads, int T, int Hs, int Ws,
+                                int wt, int wh, int ww, int d,
+                                int dtype, hipStream_t stream);
+
+/* out = Attn_G(q, k, v): the global (cross-window, same-slot) pass alone. */
+squad_status_t squad_attn_global(const void* q, const void* k, const void* v, void* out,
+                                 int B, int heads, int T, int Hs, int Ws,
+                                 int wt, int wh, int ww, int d,
+                                 int dtype, hipStream_t stream);
+
+/* out = Attn_L(q, k, Attn_G(q, k, v)): the reverse order the pages ablate
+ * (paperpeel full text, sec. 4.4 and appendix "On the ordering"). */
+squad_status_t squad_attn_fwd_reversed(const void* q, const void* k, const void* v, void* out,
+                                       int B, int heads, int T, int Hs, int Ws,
+                                       int wt, int wh, int ww, int d,
+                                       int dtype, hipStream_t stream);
+
+/* Validation only: the status any compute entry point would return for these
+ * arguments before launching (SQUAD_OK when it would launch).  Pure host
+ * function: makes no HIP call and never dereferences the pointers. */
+squad_status_t squad_attn_check(const void* q, const void* k, const void* v, const void* out,
+                                int B, int heads, int T, int Hs, int Ws,
+                                int wt, int wh, int ww, int d, int dtype);
+
+/* Largest m or N_w the kernels accept for head dim d and dtype (0 if the pair
+ * is unsupported).  Pure host function. */
+int squad_attn_max_len(int d, int dtype);
+
+/* FLOPs of one squad_attn_fwd call counting 2 per multiply-add of the two
+ * matmuls of each pass: 4*B*heads*d*n*(m + N_w) (paperpeel full text, appendix
+ * FLOP conformance paragraph: cost 4hd(nm + n^2/m)).  Returns -1 on a shape the
+ * compute entry points would reject with SQUAD_ERR_SHAPE.  Pure host function. */
+double squad_attn_flops(int B, int heads, int T, int Hs, int Ws,
+                        int wt, int wh, int ww, int d);
+
+/* Algorithmic HBM bytes of one squad_attn_fwd call as two unfused passes,
+ * each reading three [B, n, heads, d] tensors and writing one:
+ * 8*B*n*heads*d*sizeof(dtype).  -1 on a rejected shape or dtype. */
+double squad_attn_bytes(int B, int heads, int T, int Hs, int Ws,
+                        int wt, int wh, int ww, int d, int dtype);
+
+/* Static description of a status code (never NULL). */
+const char* squad_status_str(int status);
+
+/* hipError_t of the last SQUAD_ERR_HIP returned on the calling thread
+ * (0 if none). */
+int squad_attn_last_hip_error(void);
+
+/* Version of this ABI (bumped on any incompatible change). */
+int squad_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQUAD_ATTN_H */

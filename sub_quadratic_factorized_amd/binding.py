@@ -1,0 +1,166 @@
+"""ctypes binding of the SQuad-Attention C ABI (include/squad_attn.h).
+
+Argument marshalling only: every step of the operator runs in the HIP library.
+The library is loaded from this package directory; if it has not been built,
+importing the compute entry points raises instead of falling back to anything.
+
+Tensor-level functions take torch tensors laid out [B, n, heads, d] (contiguous,
+on a ROCm device, bf16 or float32) plus the latent grid (T, Hs, Ws) and window
+(wt, wh, ww).  torch is used for device memory and the current stream only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsquad_attn.so")
+
+SQUAD_BF16 = 0
+SQUAD_F32 = 1
+
+SQUAD_OK = 0
+SQUAD_ERR_NULL = 1
+SQUAD_ERR_SHAPE = 2
+SQUAD_ERR_UNSUPPORTED = 3
+SQUAD_ERR_ALIAS = 4
+SQUAD_ERR_ALIGN = 5
+SQUAD_ERR_HIP = 6
+
+COMPUTE_ENTRY_POINTS = ("squad_attn_fwd", "squad_attn_local", "squad_attn_global", "squad_attn_fwd_reversed")
+ALL_SYMBOLS = COMPUTE_ENTRY_POINTS + (
+    "squad_attn_check", "squad_attn_max_len", "squad_attn_flops", "squad_attn_bytes", "squad_status_str",
+    "squad_attn_last_hip_error", "squad_attn_abi_version",
+)
+
+_lib = None
+
+
+class SquadError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {status_str(status)} (status {status})"
+        if status == SQUAD_ERR_HIP:
+            msg += f", hipError_t {lib().squad_attn_last_hip_error()}"
+        super().__init__(msg)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument and result types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sub_quadratic_factorized_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i, d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    for name in COMPUTE_ENTRY_POINTS:
+        f = getattr(L, name)
+        f.argtypes = [p, p, p, p] + [i] * 10 + [p]
+        f.restype = i
+    L.squad_attn_check.argtypes = [p, p, p, p] + [i] * 10
+    L.squad_attn_check.restype = i
+    L.squad_attn_max_len.argtypes = [i, i]
+    L.squad_attn_max_len.restype = i
+    L.squad_attn_flops.argtypes = [i] * 9
+    L.squad_attn_flops.restype = d
+    L.squad_attn_bytes.argtypes = [i] * 10
+    L.squad_attn_bytes.restype = d
+    L.squad_status_str.argtypes = [i]
+    L.squad_status_str.restype = ctypes.c_char_p
+    L.squad_attn_last_hip_error.argtypes = []
+    L.squad_attn_last_hip_error.restype = i
+    L.squad_attn_abi_version.argtypes = []
+    L.squad_attn_abi_version.restype = i
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().squad_status_str(status).decode()
+
+
+def call_raw(name: str, q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, stream=None) -> int:
+    """Call a compute entry point with raw integer pointers; returns the status."""
+    return getattr(lib(), name)(q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, stream)
+
+
+def squad_attn_check(q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> int:
+    """Host-only validation status for raw pointer arguments (no HIP call)."""
+    return lib().squad_attn_check(q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_attn_max_len(d: int, dtype: int) -> int:
+    return lib().squad_attn_max_len(d, dtype)
+
+
+def squad_attn_flops(B, heads, T, Hs, Ws, wt, wh, ww, d) -> float:
+    return lib().squad_attn_flops(B, heads, T, Hs, Ws, wt, wh, ww, d)
+
+
+def squad_attn_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> float:
+    return lib().squad_attn_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_status_str(status: int) -> str:
+    return status_str(status)
+
+
+# ---------------------------------------------------------------------------
+# torch tensor entry points
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SQUAD_BF16
+    if t.dtype == torch.float32:
+        return SQUAD_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _call(name, q, k, v, out, grid, window, stream):
+    import torch
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_contiguous() or t.device.type != "cuda":
+            raise ValueError("q, k, v must be contiguous [B, n, heads, d] tensors on a GPU")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    B, n, heads, d = q.shape
+    T, Hs, Ws = grid
+    wt, wh, ww = window
+    if T * Hs * Ws != n:
+        raise ValueError(f"grid {tuple(grid)} has {T * Hs * Ws} tokens, tensors have n = {n}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = call_raw(name, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      B, heads, T, Hs, Ws, wt, wh, ww, d, _dtype_code(q), stream)
+    if st != SQUAD_OK:
+        raise SquadError(st, name)
+    return out
+
+
+def squad_attn_fwd(q, k, v, grid, window, out=None, stream=None):
+    """out = Attn_G(q, k, Attn_L(q, k, v)), asynchronous on the current stream."""
+    return _call("squad_attn_fwd", q, k, v, out, grid, window, stream)
+
+
+def squad_attn_local(q, k, v, grid, window, out=None, stream=None):
+    """out = Attn_L(q, k, v): the in-window pass alone."""
+    return _call("squad_attn_local", q, k, v, out, grid, window, stream)
+
+
+def squad_attn_global(q, k, v, grid, window, out=None, stream=None):
+    """out = Attn_G(q, k, v): the cross-window, same-slot pass alone."""
+    return _call("squad_attn_global", q, k, v, out, grid, window, stream)
+
+
+def squad_attn_fwd_reversed(q, k, v, grid, window, out=None, stream=None):
+    """out = Attn_L(q, k, Attn_G(q, k, v)): the reverse order."""
+    return _call("squad_attn_fwd_reversed", q, k, v, out, grid, window, stream)

@@ -1,0 +1,229 @@
+// Host side of the SQuad-Attention C ABI (declared in include/squad_attn.h):
+// argument validation (pure host code, before any HIP call), the pass
+// geometry, and the launch sequence of each entry point.
+#include "squad_attn.h"
+#include "squad_internal.h"
+
+#include <stdint.h>
+#include <string.h>
+
+namespace squad {
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+enum class Kind { kFwd, kLocal, kGlobal, kReversed };
+
+struct Problem {
+    int B, heads, T, Hs, Ws, wt, wh, ww, d, dtype;
+    int64_t n, m, nw;
+    int64_t elems;  // B*n*heads*d
+    size_t bytes;   // elems * sizeof(dtype)
+};
+
+int esize(int dtype) { return dtype == SQUAD_BF16 ? 2 : 4; }
+
+// Shape checks only: SQUAD_OK, SQUAD_ERR_SHAPE (with pr filled on success).
+// *empty is set when B == 0 or heads == 0.
+squad_status_t check_shape(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d, Problem* pr,
+                           bool* empty) {
+    *empty = false;
+    if (B < 0 || heads < 0) return SQUAD_ERR_SHAPE;
+    if (T < 1 || Hs < 1 || Ws < 1 || wt < 1 || wh < 1 || ww < 1 || d < 1) return SQUAD_ERR_SHAPE;
+    if (T % wt != 0 || Hs % wh != 0 || Ws % ww != 0) return SQUAD_ERR_SHAPE;
+    const int64_t n = (int64_t)T * Hs * Ws;  // < 2^93 is impossible: each factor < 2^31
+    if (n >= ((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;
+    const int64_t m = (int64_t)wt * wh * ww;
+    const int64_t nw = n / m;
+    pr->B = B;
+    pr->heads = heads;
+    pr->T = T;
+    pr->Hs = Hs;
+    pr->Ws = Ws;
+    pr->wt = wt;
+    pr->wh = wh;
+    pr->ww = ww;
+    pr->d = d;
+    pr->n = n;
+    pr->m = m;
+    pr->nw = nw;
+    if (B == 0 || heads == 0) {
+        *empty = true;
+        pr->elems = 0;
+        return SQUAD_OK;
+    }
+    // element count B*n*heads*d must stay below 2^62
+    const long double el = (long double)B * (long double)n * (long double)heads * (long double)d;
+    if (el >= (long double)((int64_t)1 << 62)) return SQUAD_ERR_SHAPE;
+    pr->elems = (int64_t)B * n * heads * d;
+    // every pass launches at most B*heads*max(m, N_w) problems
+    const long double probs = (long double)B * heads * (long double)(m > nw ? m : nw);
+    if (probs >= (long double)((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;
+    return SQUAD_OK;
+}
+
+bool overlaps(const void* a, const void* b, size_t bytes) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bytes && y < x + bytes;
+}
+
+squad_status_t validate(const void* q, const void* k, const void* v, const void* out, int B, int heads, int T,
+                        int Hs, int Ws, int wt, int wh, int ww, int d, int dtype, Problem* pr, bool* empty) {
+    squad_status_t s = check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, pr, empty);
+    if (s != SQUAD_OK) return s;
+    if (*empty) return SQUAD_OK;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return SQUAD_ERR_UNSUPPORTED;
+    const int maxlen = squad_attn_max_len(d, dtype);
+    if (maxlen == 0) return SQUAD_ERR_UNSUPPORTED;
+    if (pr->m > maxlen || pr->nw > maxlen) return SQUAD_ERR_UNSUPPORTED;
+    pr->dtype = dtype;
+    if (!q || !k || !v || !out) return SQUAD_ERR_NULL;
+    if ((((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)out)) & 15u) return SQUAD_ERR_ALIGN;
+    pr->bytes = (size_t)pr->elems * (size_t)esize(dtype);
+    if (overlaps(out, q, pr->bytes) || overlaps(out, k, pr->bytes)) return SQUAD_ERR_ALIAS;
+    if (out != v && overlaps(out, v, pr->bytes)) return SQUAD_ERR_ALIAS;
+    return SQUAD_OK;
+}
+
+PassGeom make_geom(const Problem& pr, bool global) {
+    PassGeom g;
+    g.n = pr.n;
+    g.heads = pr.heads;
+    g.L = (int)(global ? pr.nw : pr.m);
+    g.P = (int)(global ? pr.m : pr.nw);
+    g.nprob = (int)((int64_t)pr.B * pr.heads * g.P);
+    g.Hs = pr.Hs;
+    g.Ws = pr.Ws;
+    g.wt = pr.wt;
+    g.wh = pr.wh;
+    g.ww = pr.ww;
+    g.Cy = pr.Hs / pr.wh;
+    g.Cx = pr.Ws / pr.ww;
+    g.global = global ? 1 : 0;
+    return g;
+}
+
+hipError_t run_pass(const Problem& pr, bool global, const void* q, const void* k, const void* vals, void* out,
+                    hipStream_t st) {
+    const PassGeom g = make_geom(pr, global);
+    if (pr.dtype == SQUAD_BF16) return launch_pass_bf16(g, pr.d, q, k, vals, out, st);
+    return launch_pass_f32(g, pr.d, q, k, vals, out, st);
+}
+
+squad_status_t run(Kind kind, const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int Hs,
+                   int Ws, int wt, int wh, int ww, int d, int dtype, hipStream_t st) {
+    Problem pr;
+    bool empty = false;
+    const squad_status_t s = validate(q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, &pr, &empty);
+    if (s != SQUAD_OK || empty) return s;
+    hipError_t e = hipSuccess;
+    switch (kind) {
+        case Kind::kFwd:
+            e = run_pass(pr, false, q, k, v, out, st);
+            if (e == hipSuccess) e = run_pass(pr, true, q, k, out, out, st);
+            break;
+        case Kind::kReversed:
+            e = run_pass(pr, true, q, k, v, out, st);
+            if (e == hipSuccess) e = run_pass(pr, false, q, k, out, out, st);
+            break;
+        case Kind::kLocal:
+            e = run_pass(pr, false, q, k, v, out, st);
+            break;
+        case Kind::kGlobal:
+            e = run_pass(pr, true, q, k, v, out, st);
+            break;
+    }
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return SQUAD_ERR_HIP;
+    }
+    return SQUAD_OK;
+}
+
+}  // namespace
+
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+    if (dev < 64) cached[dev] = cus;
+    return cus;
+}
+
+}  // namespace squad
+
+extern "C" {
+
+squad_status_t squad_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int heads, int T,
+                              int Hs, int Ws, int wt, int wh, int ww, int d, int dtype, hipStream_t stream) {
+    return squad::run(squad::Kind::kFwd, q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, stream);
+}
+
+squad_status_t squad_attn_local(const void* q, const void* k, const void* v, void* out, int B, int heads, int T,
+                                int Hs, int Ws, int wt, int wh, int ww, int d, int dtype, hipStream_t stream) {
+    return squad::run(squad::Kind::kLocal, q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, stream);
+}
+
+squad_status_t squad_attn_global(const void* q, const void* k, const void* v, void* out, int B, int heads, int T,
+                                 int Hs, int Ws, int wt, int wh, int ww, int d, int dtype, hipStream_t stream) {
+    return squad::run(squad::Kind::kGlobal, q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, stream);
+}
+
+squad_status_t squad_attn_fwd_reversed(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                                       int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype,
+                                       hipStream_t stream) {
+    return squad::run(squad::Kind::kReversed, q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, stream);
+}
+
+squad_status_t squad_attn_check(const void* q, const void* k, const void* v, const void* out, int B, int heads,
+                                int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    return squad::validate(q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, &pr, &empty);
+}
+
+int squad_attn_max_len(int d, int dtype) {
+    if (d != 64 && d != 128) return 0;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return 0;
+    return squad::kMaxLen;
+}
+
+double squad_attn_flops(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d) {
+    squad::Problem pr;
+    bool empty = false;
+    if (squad::check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1.0;
+    if (empty) return 0.0;
+    return 4.0 * (double)B * heads * (double)d * (double)pr.n * (double)(pr.m + pr.nw);
+}
+
+double squad_attn_bytes(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return -1.0;
+    if (squad::check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1.0;
+    if (empty) return 0.0;
+    return 8.0 * (double)pr.elems * (double)squad::esize(dtype);
+}
+
+const char* squad_status_str(int status) {
+    switch (status) {
+        case SQUAD_OK: return "ok";
+        case SQUAD_ERR_NULL: return "null pointer argument";
+        case SQUAD_ERR_SHAPE: return "invalid shape (non-positive extent, window not tiling the grid, or size overflow)";
+        case SQUAD_ERR_UNSUPPORTED: return "unsupported dtype, head dim, or sequence length";
+        case SQUAD_ERR_ALIAS: return "output overlaps an input (only out == v is allowed)";
+        case SQUAD_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case SQUAD_ERR_HIP: return "HIP runtime or launch error";
+        default: return "unknown status";
+    }
+}
+
+int squad_attn_last_hip_error(void) { return squad::g_last_hip_error; }
+
+int squad_attn_abi_version(void) { return 1; }
+
+}  // extern "C"

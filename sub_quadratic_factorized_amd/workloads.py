@@ -29,7 +29,10 @@ tensor is the concatenation of those slices in [B, n, heads, d] layout.
 
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
+
 import numpy as np
 
 TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_BOOST = 0, 1, 2, 3
@@ -153,4 +156,40 @@ def random_geometry_inputs(B, heads, n, d, dtype, seed=0, scale=1.0):
         if dtype == "bf16":
             x = bf16_bits_to_f32(bf16_round_bits(x))
         out.append(x)
+    return tuple(out)
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 4
+    return max(1, min(16, n))
+
+
+def device_inputs(w: Workload, seed: int = 0, device: str = "cuda"):
+    """(q, k, v) as torch tensors [B, n, heads, d] on `device`, in w.dtype.
+
+    Exactly the values head_slice_f32 gives, slice by slice (generated on the
+    host in parallel threads, then copied once).
+    """
+    import torch
+    out = []
+    for tid in (TENSOR_Q, TENSOR_K, TENSOR_V):
+        if w.dtype == "bf16":
+            host = np.empty((w.B, w.n, w.heads, w.d), dtype=np.uint16)
+
+            def fill(bh, host=host, tid=tid):
+                b, h = bh
+                host[b, :, h, :] = bf16_round_bits(head_slice_f32(w, tid, b, h, seed))
+
+            with cf.ThreadPoolExecutor(_workers()) as ex:
+                list(ex.map(fill, [(b, h) for b in range(w.B) for h in range(w.heads)]))
+            out.append(torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).to(device))
+        else:
+            host = np.empty((w.B, w.n, w.heads, w.d), dtype=np.float32)
+            for b in range(w.B):
+                for h in range(w.heads):
+                    host[b, :, h, :] = head_slice_f32(w, tid, b, h, seed)
+            out.append(torch.from_numpy(host).to(device))
     return tuple(out)

@@ -1,0 +1,55 @@
+"""Shared helpers for the GPU parity tests: seeded inputs on the device and the
+comparison metrics.  Inputs come from sub_quadratic_factorized_amd.workloads
+(the same generator feeds the oracle); expected values come from the oracle."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from sub_quadratic_factorized_amd import workloads as wl
+
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 5e-3
+F32_REL_L2 = 1e-5
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def workload_device_inputs(w: wl.Workload, seed: int = 0):
+    """(q, k, v) device tensors [B, n, heads, d] for a named workload."""
+    return wl.device_inputs(w, seed)
+
+
+def host_to_device(arrs, dtype):
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    return tuple(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(tdt) for a in arrs)
+
+
+def to_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    max_abs = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    den = float(np.linalg.norm(ref.ravel()))
+    rel = float(np.linalg.norm((got - ref).ravel()) / den) if den > 0 else max_abs
+    return max_abs, rel
+
+
+def assert_close(got, ref, dtype, what=""):
+    max_abs, rel = errors(got, ref)
+    log(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    if dtype == "bf16":
+        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (what, max_abs, rel)
+    else:
+        assert rel <= F32_REL_L2, (what, max_abs, rel)
+    return max_abs, rel

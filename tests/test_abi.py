@@ -1,0 +1,174 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects every invalid argument on the host before any HIP
+call (so fake pointers are safe here)."""
+
+import os
+import re
+
+import pytest
+
+from sub_quadratic_factorized_amd import binding as bd
+from oracle import squad_oracle as so
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "squad_attn.h")
+
+# a valid geometry: the 5B native shape
+GEO = dict(B=1, heads=24, T=21, Hs=22, Ws=40, wt=21, wh=2, ww=4, d=128)
+BYTES = 1 * 18480 * 24 * 128 * 2
+A = 1 << 40  # fake, well separated, 16-byte aligned addresses
+Q, K, V, O = A, A + 4 * BYTES, A + 8 * BYTES, A + 12 * BYTES
+
+
+def call(name="squad_attn_fwd", q=Q, k=K, v=V, out=O, dtype=bd.SQUAD_BF16, **over):
+    g = dict(GEO)
+    g.update(over)
+    return bd.call_raw(name, q, k, v, out, g["B"], g["heads"], g["T"], g["Hs"], g["Ws"],
+                       g["wt"], g["wh"], g["ww"], g["d"], dtype)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(squad_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = bd.lib()
+    names = declared_functions()
+    assert set(bd.ALL_SYMBOLS) == set(names)
+    for n in names:
+        assert getattr(lib, n) is not None
+    assert lib.squad_attn_abi_version() == 1
+
+
+def test_exports_via_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", bd.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (squad_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+@pytest.mark.parametrize("name", bd.COMPUTE_ENTRY_POINTS)
+def test_shape_errors(name):
+    S = bd.SQUAD_ERR_SHAPE
+    assert call(name, B=-1) == S
+    assert call(name, heads=-2) == S
+    for key in ("T", "Hs", "Ws", "wt", "wh", "ww", "d"):
+        assert call(name, **{key: 0}) == S, key
+        assert call(name, **{key: -3}) == S, key
+    assert call(name, wh=3) == S                    # 22 % 3 != 0
+    assert call(name, ww=3) == S                    # 40 % 3 != 0
+    assert call(name, wt=4) == S                    # 21 % 4 != 0
+    assert call(name, T=1 << 16, Hs=1 << 16, Ws=1, wt=1, wh=1, ww=1) == S  # n >= 2^31
+    # element count overflow (B*n*heads*d >= 2^62)
+    assert call(name, B=1 << 30, heads=1 << 30, T=1 << 10, Hs=1, Ws=1, wt=1, wh=1, ww=1) == S
+    # problem count beyond a 31-bit grid
+    assert call(name, B=1 << 20, heads=1 << 10, T=512, Hs=1, Ws=1, wt=1, wh=1, ww=1, d=64) == S
+
+
+@pytest.mark.parametrize("name", bd.COMPUTE_ENTRY_POINTS)
+def test_unsupported(name):
+    U = bd.SQUAD_ERR_UNSUPPORTED
+    assert call(name, dtype=7) == U
+    assert call(name, dtype=-1) == U
+    assert call(name, d=96) == U
+    assert call(name, d=256) == U
+    assert call(name, d=32) == U
+    # window of 1024 tokens > max length
+    assert call(name, T=4, Hs=16, Ws=16, wt=4, wh=16, ww=16) == U
+    # 1024 windows of one token: N_w > max length
+    assert call(name, T=4, Hs=16, Ws=16, wt=1, wh=1, ww=1) == U
+    # shape errors win over unsupported (documented order)
+    assert call(name, d=96, wh=3) == bd.SQUAD_ERR_SHAPE
+
+
+@pytest.mark.parametrize("name", bd.COMPUTE_ENTRY_POINTS)
+def test_null_align_alias(name):
+    assert call(name, q=0) == bd.SQUAD_ERR_NULL
+    assert call(name, k=0) == bd.SQUAD_ERR_NULL
+    assert call(name, v=0) == bd.SQUAD_ERR_NULL
+    assert call(name, out=0) == bd.SQUAD_ERR_NULL
+    assert call(name, q=0, dtype=9) == bd.SQUAD_ERR_UNSUPPORTED  # order: unsupported before null
+    for key in ("q", "k", "v", "out"):
+        for off in (2, 8):
+            assert call(name, **{key: {"q": Q, "k": K, "v": V, "out": O}[key] + off}) == bd.SQUAD_ERR_ALIGN
+    assert call(name, q=0, out=O + 8) == bd.SQUAD_ERR_NULL       # order: null before align
+    assert call(name, out=Q) == bd.SQUAD_ERR_ALIAS
+    assert call(name, out=K + 16) == bd.SQUAD_ERR_ALIAS
+    assert call(name, out=Q - BYTES + 16) == bd.SQUAD_ERR_ALIAS  # tail of out overlaps head of q
+    assert call(name, out=V + 16) == bd.SQUAD_ERR_ALIAS          # partial overlap with v
+    assert call(name, out=V - 16) == bd.SQUAD_ERR_ALIAS
+    assert call(name, out=K - BYTES, dtype=bd.SQUAD_F32) == bd.SQUAD_ERR_ALIAS  # f32 buffers are twice as long
+
+
+def check(q=Q, k=K, v=V, out=O, dtype=bd.SQUAD_BF16, **over):
+    g = dict(GEO)
+    g.update(over)
+    return bd.squad_attn_check(q, k, v, out, g["B"], g["heads"], g["T"], g["Hs"], g["Ws"],
+                               g["wt"], g["wh"], g["ww"], g["d"], dtype)
+
+
+def test_check_accepts_what_would_launch():
+    assert check() == bd.SQUAD_OK
+    assert check(out=V) == bd.SQUAD_OK                 # in place over v
+    assert check(out=Q + BYTES) == bd.SQUAD_OK         # adjacent buffers do not overlap
+    assert check(out=Q - BYTES) == bd.SQUAD_OK
+    assert check(dtype=bd.SQUAD_F32, out=Q + 2 * BYTES) == bd.SQUAD_OK
+    assert check(dtype=bd.SQUAD_F32, out=Q + BYTES) == bd.SQUAD_ERR_ALIAS
+    assert check(d=64) == bd.SQUAD_OK
+    assert check(T=8, Hs=8, Ws=8, wt=8, wh=8, ww=8) == bd.SQUAD_OK      # one window of 512
+    assert check(T=8, Hs=8, Ws=8, wt=1, wh=1, ww=1) == bd.SQUAD_OK      # 512 windows of one token
+    assert check(T=8, Hs=8, Ws=16, wt=8, wh=8, ww=16) == bd.SQUAD_ERR_UNSUPPORTED
+    assert check(B=0, q=0) == bd.SQUAD_OK
+
+
+@pytest.mark.parametrize("name", bd.COMPUTE_ENTRY_POINTS)
+def test_check_matches_entry_points_on_rejections(name):
+    cases = [dict(B=-1), dict(wh=3), dict(d=96), dict(dtype=4), dict(q=0), dict(out=O + 4), dict(out=K + 32),
+             dict(B=0, q=0)]
+    for c in cases:
+        assert call(name, **c) == check(**c), c
+
+
+@pytest.mark.parametrize("name", bd.COMPUTE_ENTRY_POINTS)
+def test_empty_problem_is_a_noop(name):
+    assert call(name, B=0, q=0, k=0, v=0, out=0) == bd.SQUAD_OK
+    assert call(name, heads=0, q=0, k=0, v=0, out=0) == bd.SQUAD_OK
+    assert call(name, B=0, wh=3) == bd.SQUAD_ERR_SHAPE
+
+
+def test_max_len():
+    for d in (64, 128):
+        for dt in (bd.SQUAD_BF16, bd.SQUAD_F32):
+            assert bd.squad_attn_max_len(d, dt) == 512
+    assert bd.squad_attn_max_len(96, bd.SQUAD_BF16) == 0
+    assert bd.squad_attn_max_len(128, 5) == 0
+
+
+def test_flops_and_bytes_helpers():
+    from sub_quadratic_factorized_amd import workloads as wl
+    for w in wl.WORKLOADS.values():
+        f = bd.squad_attn_flops(*w.geometry())
+        assert f == so.squad_flops(*w.geometry())
+        es = 2 if w.dtype == "bf16" else 4
+        dt = bd.SQUAD_BF16 if w.dtype == "bf16" else bd.SQUAD_F32
+        assert bd.squad_attn_bytes(*w.geometry(), dt) == 8 * w.B * w.n * w.heads * w.d * es
+    assert bd.squad_attn_flops(1, 24, 21, 22, 40, 21, 2, 4, 128) == 63_128_862_720
+    assert bd.squad_attn_flops(1, 24, 21, 22, 40, 21, 3, 4, 128) == -1
+    assert bd.squad_attn_bytes(1, 24, 21, 22, 40, 21, 2, 4, 128, 9) == -1
+    assert bd.squad_attn_flops(0, 24, 21, 22, 40, 21, 2, 4, 128) == 0
+
+
+def test_status_strings():
+    for s in range(7):
+        assert isinstance(bd.status_str(s), str) and bd.status_str(s)
+    assert bd.status_str(123) == "unknown status"
+    assert bd.lib().squad_attn_last_hip_error() == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(bd, "_lib", None)
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        bd.lib()

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+Bars: bf16 storage with fp32 accumulation -> max |err| <= 2e-2 and relative L2
+error <= 5e-3; the float32 path -> relative L2 error <= 1e-5.  Small cases are
+compared element by element over the whole output; the full-size workloads
+are run whole on the GPU and compared on sampled (batch, head) slices, each of
+which the oracle computes independently (heads never interact).
+"""
+
+import numpy as np
+import pytest
+
+from oracle import squad_oracle as so
+from sub_quadratic_factorized_amd import binding as bd
+from sub_quadratic_factorized_amd import workloads as wl
+
+from gpu_common import assert_close, host_to_device, log, to_f64, workload_device_inputs
+
+pytestmark = pytest.mark.gpu
+
+OPS = {
+    "fwd": (bd.squad_attn_fwd, so.squad_attention),
+    "local": (bd.squad_attn_local, so.local_pass),
+    "global": (bd.squad_attn_global, so.global_pass),
+    "reversed": (bd.squad_attn_fwd_reversed, so.squad_attention_reversed),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def run_small(geo, dtype, op="fwd", seed=0, qk_scale=1.0, B=1, heads=2, d=64):
+    T, Hs, Ws, wt, wh, ww = geo
+    n = T * Hs * Ws
+    log(f"case op={op} dtype={dtype} B={B} heads={heads} d={d} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} "
+        f"qk_scale={qk_scale}")
+    q, k, v = wl.random_geometry_inputs(B, heads, n, d, dtype, seed=seed)
+    if qk_scale != 1.0:
+        # larger logits; values stay N(0, 1) so the absolute error bar keeps its meaning
+        q, k = (wl.bf16_bits_to_f32(wl.bf16_round_bits(x * np.float32(qk_scale))) if dtype == "bf16"
+                else x * np.float32(qk_scale) for x in (q, k))
+    qd, kd, vd = host_to_device((q, k, v), dtype)
+    gpu_fn, ref_fn = OPS[op]
+    out = gpu_fn(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww))
+    ref = ref_fn(q, k, v, (B, heads, T, Hs, Ws, wt, wh, ww, d))
+    return assert_close(to_f64(out), ref, dtype, op)
+
+
+# ---------------------------------------------------------------------------
+# The tiny fp32 workload (both readings of its value recipe)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_prescaled"])
+@pytest.mark.parametrize("op", list(OPS))
+def test_tiny_workload_f32(name, op):
+    w = wl.WORKLOADS[name]
+    log(f"case workload={name} op={op}")
+    q, k, v = wl.full_inputs_f32(w)
+    qd, kd, vd = host_to_device((q, k, v), "f32")
+    gpu_fn, ref_fn = OPS[op]
+    out = gpu_fn(qd, kd, vd, (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww))
+    assert_close(to_f64(out), ref_fn(q, k, v, w.geometry()), "f32", f"{name}/{op}")
+
+
+@pytest.mark.parametrize("op", list(OPS))
+def test_tiny_geometry_bf16(op):
+    run_small((3, 4, 4, 3, 2, 2), "bf16", op)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled heads
+# ---------------------------------------------------------------------------
+
+SAMPLES = {
+    "wan5b_704p": [(0, 0), (0, 11), (0, 23)],
+    "wan1p3b_480p": [(0, 0), (0, 7)],
+    "wan5b_4x": [(0, 0), (0, 19)],
+    "wan14b_4x_cfg": [(0, 3), (1, 39)],
+}
+
+
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_workload_bf16_sampled_heads(name):
+    import torch
+    w = wl.WORKLOADS[name]
+    log(f"case workload={name} op=fwd (generating inputs)")
+    qd, kd, vd = workload_device_inputs(w)
+    out = bd.squad_attn_fwd(qd, kd, vd, (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww))
+    torch.cuda.synchronize()
+    table = so.window_slot_table(w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
+    for b, h in SAMPLES[name]:
+        q, k, v = wl.head_slices_f64(w, b, h)
+        ref = so.squad_head(q, k, v, table)
+        assert_close(to_f64(out[b, :, h, :]), ref, "bf16", f"{name} b={b} h={h}")
+    del qd, kd, vd, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("op", ["local", "global", "reversed"])
+def test_headline_workload_each_pass(op):
+    import torch
+    w = wl.WORKLOADS["wan5b_704p"]
+    log(f"case workload=wan5b_704p op={op}")
+    qd, kd, vd = workload_device_inputs(w)
+    out = OPS[op][0](qd, kd, vd, (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww))
+    torch.cuda.synchronize()
+    table = so.window_slot_table(w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
+    head_fn = {"local": so.local_pass_head, "global": so.global_pass_head, "reversed": so.squad_reversed_head}[op]
+    for b, h in [(0, 5), (0, 17)]:
+        q, k, v = wl.head_slices_f64(w, b, h)
+        assert_close(to_f64(out[b, :, h, :]), head_fn(q, k, v, table), "bf16", f"{op} h={h}")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases: ragged lengths on every launch configuration, extremes, layouts
+# ---------------------------------------------------------------------------
+
+# (T, Hs, Ws, wt, wh, ww): m = wt*wh*ww, N_w = n/m
+RAGGED = [
+    (1, 6, 10, 1, 3, 5),      # m=15  N_w=4
+    (3, 10, 12, 3, 2, 2),     # m=12  N_w=30
+    (2, 9, 34, 1, 1, 17),     # m=17  N_w=36
+    (1, 11, 99, 1, 1, 33),    # m=33  N_w=33
+    (4, 5, 60, 2, 5, 10),     # m=100 N_w=12
+    (2, 14, 100, 2, 1, 100),  # m=200 N_w=14
+    (1, 7, 600, 1, 1, 200),   # m=200 N_w=21 (13 tiles)
+    (2, 5, 300, 1, 1, 300),   # m=300 N_w=10 (19 tiles)
+    (1, 4, 800, 1, 1, 400),   # m=400 N_w=8  (25 tiles)
+    (1, 3, 330, 1, 3, 1),     # m=3   N_w=330
+]
+
+
+@pytest.mark.parametrize("geo", RAGGED, ids=[f"m{g[3]*g[4]*g[5]}_nw{g[0]*g[1]*g[2]//(g[3]*g[4]*g[5])}" for g in RAGGED])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_lengths(geo, dtype):
+    run_small(geo, dtype, "fwd", heads=2, d=128 if dtype == "bf16" else 64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_head_dims(dtype, d):
+    run_small((3, 4, 8, 3, 2, 2), dtype, "fwd", heads=3, d=d, B=2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_window_is_full_attention(dtype):
+    # N_w = 1, m = 512 (the longest local problem)
+    run_small((8, 8, 8, 8, 8, 8), dtype, "fwd", heads=1, d=64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_token_windows(dtype):
+    # m = 1, N_w = 512 (the longest global problem)
+    run_small((8, 8, 8, 1, 1, 1), dtype, "fwd", heads=1, d=64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_both_lengths_at_maximum_region(dtype):
+    # m = 512 with N_w = 64, then m = 64 with N_w = 512
+    run_small((8, 64, 64, 8, 8, 8), dtype, "fwd", heads=1, d=64)
+    run_small((8, 64, 64, 1, 8, 8), dtype, "fwd", heads=1, d=64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_logits(dtype):
+    # logit std ~ 9 (Q, K scaled by 3): the running maximum is refreshed many times
+    run_small((3, 10, 12, 3, 2, 2), dtype, "fwd", qk_scale=3.0, d=128)
+    run_small((2, 14, 100, 2, 1, 100), dtype, "fwd", qk_scale=3.0, d=128)
+    run_small((1, 4, 800, 1, 1, 400), dtype, "fwd", qk_scale=3.0, d=64)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_in_place_equals_out_of_place(dtype):
+    import torch
+    geo = (3, 10, 12, 3, 2, 2)
+    T, Hs, Ws, wt, wh, ww = geo
+    q, k, v = wl.random_geometry_inputs(1, 4, T * Hs * Ws, 128, dtype, seed=7)
+    qd, kd, vd = host_to_device((q, k, v), dtype)
+    for fn in (bd.squad_attn_local, bd.squad_attn_global, bd.squad_attn_fwd, bd.squad_attn_fwd_reversed):
+        ref = fn(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww))
+        buf = vd.clone()
+        fn(qd, kd, buf, (T, Hs, Ws), (wt, wh, ww), out=buf)
+        torch.cuda.synchronize()
+        assert torch.equal(buf, ref), fn.__name__
+
+
+def test_deterministic():
+    import torch
+    w = wl.WORKLOADS["wan5b_704p"]
+    qd, kd, vd = workload_device_inputs(w)
+    a = bd.squad_attn_fwd(qd, kd, vd, (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww))
+    b = bd.squad_attn_fwd(qd, kd, vd, (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww))
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_empty_batch_is_noop():
+    import torch
+    q = torch.empty((0, 48, 2, 64), device="cuda", dtype=torch.bfloat16)
+    out = bd.squad_attn_fwd(q, q.clone(), q.clone(), (3, 4, 4), (3, 2, 2))
+    assert out.shape == q.shape
+
+
+def test_rejections_raise():
+    import torch
+    q = torch.zeros((1, 48, 2, 64), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(bd.SquadError) as e:
+        bd.squad_attn_fwd(q, q.clone(), q.clone(), (3, 4, 4), (3, 3, 2))
+    assert e.value.status == bd.SQUAD_ERR_SHAPE
+    with pytest.raises(bd.SquadError) as e:
+        bd.squad_attn_fwd(q, q, q.clone(), (3, 4, 4), (3, 2, 2), out=q)
+    assert e.value.status == bd.SQUAD_ERR_ALIAS
