@@ -74,7 +74,7 @@ def traffic_from_profile(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s=20.0):
+def cpu_baseline(w, min_s=10.0, budget_s=25.0):
     """The fp64 oracle on host cores over a bounded sample of the workload's heads."""
     import numpy as np
     from oracle import squad_oracle as so
@@ -85,26 +85,29 @@ def cpu_baseline(w, budget_s=20.0):
     except Exception:  # pragma: no cover - threadpoolctl is optional
         threads = 1
     table = so.window_slot_table(w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
-    heads_done, elapsed = 0, 0.0
     per_head_flops = so.squad_flops(1, 1, w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww, w.d)
     q, k, v = wl.head_slices_f64(w, 0, 0)
     so.squad_head(q, k, v, table)  # warm-up, untimed
-    for h in range(w.heads):
-        q, k, v = wl.head_slices_f64(w, 0, h)
-        t0 = time.perf_counter()
-        so.squad_head(q, k, v, table)
-        elapsed += time.perf_counter() - t0
-        heads_done += 1
-        if elapsed > budget_s:
-            break
+    # whole sweeps over the heads of batch element 0, repeated until ~min_s of work
+    heads_done, elapsed, sweeps = 0, 0.0, 0
+    while elapsed < min_s and elapsed < budget_s:
+        for h in range(w.heads):
+            q, k, v = wl.head_slices_f64(w, 0, h)
+            t0 = time.perf_counter()
+            so.squad_head(q, k, v, table)
+            elapsed += time.perf_counter() - t0
+            heads_done += 1
+            if elapsed > budget_s:
+                break
+        sweeps += 1
     rate = heads_done * per_head_flops / elapsed / 1e12
     return {
         "value": rate,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{heads_done} of {w.heads} heads (b=0) of {w.name}, numpy float64, "
-                  f"{elapsed:.2f} s; scaled per head ({w.name} has {w.B * w.heads} (b, head) slices)",
+        "sample": f"{heads_done} (b=0, head) slices of {w.name} ({sweeps} sweep(s) over its {w.heads} heads), "
+                  f"numpy float64, {elapsed:.2f} s of oracle time",
         "ms_per_block_equiv": elapsed / heads_done * w.B * w.heads * 1e3,
     }
 
@@ -117,6 +120,8 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the 5B 704p block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=100)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for scaling hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -227,6 +232,15 @@ def main():
         "baseline_context": {"pages_ms_per_block": PAGES_MS_PER_BLOCK, "hardware": "NVIDIA H100 80GB (pages)"},
         "kernel_source_hash": kernel_source_hash(),
     }
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = nbytes
+        del src, dst
     if not args.no_cpu_baseline:
         eprint("[bench] timing the oracle on host cores (bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -4,6 +4,8 @@ comparison metrics.  Inputs come from sub_quadratic_factorized_amd.workloads
 
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -45,11 +47,31 @@ def errors(got, ref):
     return max_abs, rel
 
 
-def assert_close(got, ref, dtype, what=""):
+def _record(entry):
+    path = os.environ.get("PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(entry) + "\n")
+
+
+def assert_close(got, ref, dtype, what="", magnitude_scaled=False):
+    """Check the parity bar.
+
+    bf16: max |got - ref| <= 2e-2 and rel-L2 <= 5e-3.  With magnitude_scaled the
+    absolute bar applies to |got - ref| / max(1, |ref|): bf16 storage of Y and O
+    has a half-ulp of 2^-9 |x|, so outputs beyond 1 in magnitude (sharp
+    attention copying single values) need the bar scaled with them.
+    float32: rel-L2 <= 1e-5.
+    """
     max_abs, rel = errors(got, ref)
-    log(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    scaled = max_abs
+    if magnitude_scaled:
+        scaled = float(np.max(np.abs(np.asarray(got) - ref) / np.maximum(1.0, np.abs(ref))))
+    log(f"  {what}: max_abs={max_abs:.3e} scaled={scaled:.3e} rel_l2={rel:.3e} max|ref|={np.max(np.abs(ref)):.3f}")
+    _record({"case": what, "dtype": dtype, "max_abs": max_abs, "scaled_max": scaled, "rel_l2": rel,
+             "max_ref": float(np.max(np.abs(ref))), "magnitude_scaled": magnitude_scaled})
     if dtype == "bf16":
-        assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (what, max_abs, rel)
+        assert scaled <= BF16_MAX_ABS and rel <= BF16_REL_L2, (what, max_abs, scaled, rel)
     else:
         assert rel <= F32_REL_L2, (what, max_abs, rel)
     return max_abs, rel

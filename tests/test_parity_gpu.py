@@ -35,7 +35,8 @@ def _gpu():
     bd.lib()
 
 
-def run_small(geo, dtype, op="fwd", seed=0, qk_scale=1.0, B=1, heads=2, d=64):
+def run_small(geo, dtype, op="fwd", seed=0, qk_scale=1.0, B=1, heads=2, d=64, key_ramp=0.0,
+              magnitude_scaled=False):
     T, Hs, Ws, wt, wh, ww = geo
     n = T * Hs * Ws
     log(f"case op={op} dtype={dtype} B={B} heads={heads} d={d} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} "
@@ -45,11 +46,20 @@ def run_small(geo, dtype, op="fwd", seed=0, qk_scale=1.0, B=1, heads=2, d=64):
         # larger logits; values stay N(0, 1) so the absolute error bar keeps its meaning
         q, k = (wl.bf16_bits_to_f32(wl.bf16_round_bits(x * np.float32(qk_scale))) if dtype == "bf16"
                 else x * np.float32(qk_scale) for x in (q, k))
+    if key_ramp:
+        # keys grow along the grid's x axis, which runs inside every window and
+        # across windows, so later key blocks of a problem hold larger logits
+        # and the running maximum must be refreshed
+        x = np.arange(n, dtype=np.float32) % Ws
+        ramp = (1.0 + key_ramp * x / Ws)[None, :, None, None]
+        k = k * ramp
+        if dtype == "bf16":
+            k = wl.bf16_bits_to_f32(wl.bf16_round_bits(k))
     qd, kd, vd = host_to_device((q, k, v), dtype)
     gpu_fn, ref_fn = OPS[op]
     out = gpu_fn(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww))
     ref = ref_fn(q, k, v, (B, heads, T, Hs, Ws, wt, wh, ww, d))
-    return assert_close(to_f64(out), ref, dtype, op)
+    return assert_close(to_f64(out), ref, dtype, op, magnitude_scaled=magnitude_scaled)
 
 
 # ---------------------------------------------------------------------------
@@ -168,11 +178,21 @@ def test_both_lengths_at_maximum_region(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_large_logits(dtype):
-    # logit std ~ 9 (Q, K scaled by 3): the running maximum is refreshed many times
-    run_small((3, 10, 12, 3, 2, 2), dtype, "fwd", qk_scale=3.0, d=128)
-    run_small((2, 14, 100, 2, 1, 100), dtype, "fwd", qk_scale=3.0, d=128)
-    run_small((1, 4, 800, 1, 1, 400), dtype, "fwd", qk_scale=3.0, d=64)
+def test_sharp_attention(dtype):
+    # logit std ~ 9 (Q, K scaled by 3): near one-hot rows copy single values,
+    # so outputs reach max|V|; the absolute bar is applied relative to |O|
+    run_small((3, 10, 12, 3, 2, 2), dtype, "fwd", qk_scale=3.0, d=128, magnitude_scaled=True)
+    run_small((2, 14, 100, 2, 1, 100), dtype, "fwd", qk_scale=3.0, d=128, magnitude_scaled=True)
+    run_small((1, 4, 800, 1, 1, 400), dtype, "fwd", qk_scale=3.0, d=64, magnitude_scaled=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_running_maximum_refresh(dtype):
+    # logits rise along each problem's rows: every few key blocks the block
+    # maximum exceeds the running one by more than the refresh headroom
+    run_small((1, 4, 800, 1, 1, 400), dtype, "fwd", qk_scale=1.5, key_ramp=3.0, d=64, magnitude_scaled=True)
+    run_small((2, 14, 100, 2, 1, 100), dtype, "local", qk_scale=1.5, key_ramp=3.0, d=128, magnitude_scaled=True)
+    run_small((1, 3, 330, 1, 3, 1), dtype, "global", qk_scale=1.5, key_ramp=3.0, d=128, magnitude_scaled=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
