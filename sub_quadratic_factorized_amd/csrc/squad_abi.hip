@@ -101,6 +101,12 @@ PassGeom make_geom(const Problem& pr, bool global) {
     g.Cy = pr.Hs / pr.wh;
     g.Cx = pr.Ws / pr.ww;
     g.global = global ? 1 : 0;
+    g.div_heads = make_fastdiv((uint32_t)g.heads);
+    g.div_P = make_fastdiv((uint32_t)g.P);
+    g.div_wins_t = make_fastdiv((uint32_t)(g.Cy * g.Cx));
+    g.div_Cx = make_fastdiv((uint32_t)g.Cx);
+    g.div_slots_t = make_fastdiv((uint32_t)(pr.wh * pr.ww));
+    g.div_ww = make_fastdiv((uint32_t)pr.ww);
     return g;
 }
 

@@ -10,6 +10,30 @@ namespace squad {
 // any kernel instance accepts.
 constexpr int kMaxLen = 512;
 
+// Exact unsigned division of 0 <= n < 2^31 by a fixed 1 <= d < 2^31 with one
+// multiply and shift (Granlund & Montgomery, "Division by invariant integers
+// using multiplication", 1994, thm. 4.2 with N = 31): with 2^(l-1) < d <= 2^l,
+// m = floor(2^(31+l) / d) + 1 < 2^32 + 1 and q = floor(n * m / 2^(31+l)).
+struct FastDiv {
+    uint64_t m;
+    uint32_t shift;  // 31 + l
+    uint32_t d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    FastDiv f;
+    f.d = d;
+    f.shift = 31 + l;
+    f.m = ((1ull << (31 + l)) / d) + 1;
+    return f;
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    return (uint32_t)(((uint64_t)n * f.m) >> f.shift);
+}
+
 // One pass seen as a batch of independent softmax attentions ("problems").
 //
 // The local pass has B*heads*N_w problems: (b, h, window c), each over the
@@ -29,15 +53,18 @@ struct PassGeom {
     int wt, wh, ww; // window extents
     int Cy, Cx;     // windows along y and x
     int global;     // 0: local pass, 1: global pass
+    // divisors of the problem decode and of the row maps
+    FastDiv div_heads, div_P;         // problem -> (b, pi, h)
+    FastDiv div_wins_t, div_Cx;       // window c -> (ct, cy, cx): Cy*Cx, Cx
+    FastDiv div_slots_t, div_ww;      // slot j -> (jt, jy, jx): wh*ww, ww
 };
 
 // Token index of slot 0 of window c (windows numbered row-major over their
 // tile coordinates (ct, cy, cx)).
 __host__ __device__ inline int win_origin(const PassGeom& g, int c) {
-    const int per_t = g.Cy * g.Cx;
-    const int ct = c / per_t;
-    const int r = c - ct * per_t;
-    const int cy = r / g.Cx;
+    const int ct = (int)fdiv((uint32_t)c, g.div_wins_t);
+    const int r = c - ct * (int)g.div_wins_t.d;
+    const int cy = (int)fdiv((uint32_t)r, g.div_Cx);
     const int cx = r - cy * g.Cx;
     return ((ct * g.wt) * g.Hs + cy * g.wh) * g.Ws + cx * g.ww;
 }
@@ -45,12 +72,23 @@ __host__ __device__ inline int win_origin(const PassGeom& g, int c) {
 // Offset, in tokens, of in-window slot j (slots numbered row-major over the
 // in-window offset (jt, jy, jx)).
 __host__ __device__ inline int slot_offset(const PassGeom& g, int j) {
-    const int per_t = g.wh * g.ww;
-    const int jt = j / per_t;
-    const int r = j - jt * per_t;
-    const int jy = r / g.ww;
+    const int jt = (int)fdiv((uint32_t)j, g.div_slots_t);
+    const int r = j - jt * (int)g.div_slots_t.d;
+    const int jy = (int)fdiv((uint32_t)r, g.div_ww);
     const int jx = r - jy * g.ww;
     return (jt * g.Hs + jy) * g.Ws + jx;
+}
+
+// (b, pi, h) of problem p: heads vary fastest, then the problem index within
+// the (b, h) slice, then the batch element.
+struct ProblemIndex {
+    int b, pi, h;
+};
+
+__host__ __device__ inline ProblemIndex decode_problem(const PassGeom& g, int p) {
+    const int t = (int)fdiv((uint32_t)p, g.div_heads);
+    const int b = (int)fdiv((uint32_t)t, g.div_P);
+    return ProblemIndex{b, t - b * g.P, p - t * g.heads};
 }
 
 // Kernel launchers.  Each validates nothing (the ABI layer did) and returns the

@@ -30,13 +30,9 @@ __global__ __launch_bounds__(64 * NWAVE) void pass_f32_kernel(PassGeom g, const 
     const int L = g.L;
     const int row_stride = g.heads * D;
 
-    const int p = blockIdx.x;
-    const int h = p % g.heads;
-    const int t = p / g.heads;
-    const int pi = t % g.P;
-    const int b = t / g.P;
-    const int base = g.global ? slot_offset(g, pi) : win_origin(g, pi);
-    const int64_t poff = ((int64_t)b * g.n + base) * row_stride + (int64_t)h * D;
+    const ProblemIndex pr = decode_problem(g, blockIdx.x);
+    const int base = g.global ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
+    const int64_t poff = ((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D;
 
     for (int r = tid; r < L; r += blockDim.x) tab[r] = g.global ? win_origin(g, r) : slot_offset(g, r);
     __syncthreads();
