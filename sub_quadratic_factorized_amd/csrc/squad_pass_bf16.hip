@@ -28,6 +28,7 @@
 //     refreshed running maximum (refreshed only when a block's maximum exceeds
 //     it by more than 2^8), so the accumulator rescale is rare and P <= 256.
 #include "squad_internal.h"
+#include "squad_layout.h"
 
 #include <mutex>
 
@@ -41,25 +42,11 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int BR = 32;                    // rows per streamed block
+constexpr int BR = kBlockRows;
 constexpr float kRescaleHeadroom = 8.0f;  // log2 units
 
 template <int D>
-struct Geo {
-    static constexpr int KC = D / 8;     // 16-byte chunks per row
-    static constexpr int NCH = BR * KC;  // chunks per block = threads that stage one
-    static constexpr int KS = D / 32;    // k-steps of the score MFMA
-    static constexpr int DT = D / 16;    // 16-row d tiles of the output
-    // K and Q rows padded by 16 B: the 16 rows read by one operand fetch start
-    // 4 banks apart.  V rows padded by 64 B: the 4 rows x 4 pieces read by one
-    // transposing fetch land on 16 distinct bank pairs.
-    static constexpr int KSTR = D + 8;
-    static constexpr int VSTR = D + 32;
-};
-
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
+using Geo = BlockGeo<D>;
 
 // Maximum over the four lanes {l, l^16, l^32, l^48} that share a query row in
 // the transposed score layout (two half-wave swaps, no LDS traffic).
@@ -78,10 +65,12 @@ __device__ __forceinline__ float row_max4(float x) {
 // for; LMAX: longest problem of this instance (sizes the LDS Q stage); QSTAGE:
 // stream Q through the LDS stage (else each wave loads its Q tiles straight
 // into registers at a problem's first step, for problems too long to stage).
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE>
-__global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void pass_bf16_kernel(
-    PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
-    float scale_log2) {
+// GP: the global pass (rows of a problem are windows at one slot) rather than
+// the local pass (rows are the slots of one window).
+template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP>
+__device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __restrict__ qp,
+                                          const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
+                                          float scale_log2) {
     using G = Geo<D>;
     static_assert(PD % 2 == 0, "the LDS buffer of a step must be known at compile time");
     constexpr int QROWS = QSTAGE ? (LMAX + BR - 1) / BR * BR : 1;
@@ -91,13 +80,16 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))
     __shared__ int tab[LMAX];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int L = g.L;
     const int NB = (L + BR - 1) / BR;
     const int ntiles = (L + 15) / 16;
+    // waves past the last tile only stage data; a wave's partial tiles compute
+    // on clamped rows and are never stored
+    const bool computes = wave * QT < ntiles;
     const int nmine = (g.nprob - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int total = nmine * NB;  // steps
     const int row_stride = g.heads * D;
@@ -110,12 +102,12 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))
 
     // row r of any problem of this pass sits at a fixed token offset from the
     // problem's base token
-    for (int r = tid; r < L; r += blockDim.x) tab[r] = g.global ? win_origin(g, r) : slot_offset(g, r);
+    for (int r = tid; r < L; r += blockDim.x) tab[r] = GP ? win_origin(g, r) : slot_offset(g, r);
     __syncthreads();
 
     auto prob_offset = [&](int it) -> int64_t {
         const ProblemIndex pr = decode_problem(g, (int)blockIdx.x + it * (int)gridDim.x);
-        const int base = g.global ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
+        const int base = GP ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
         return ((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D;
     };
 
@@ -126,29 +118,39 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))
     // stored) and past-the-end problems to the last one (never consumed).
     u32x4 sk[PD], sv[PD], sq[PD];
     int ld_it = 0, ld_b = 0;
+    // loads of steps past the last problem, and of Q past the last problem,
+    // all read the first 16 bytes of the tensor (one cached line, never used)
+    bool ld_dead = nmine <= 0;
+    bool q_dead = nmine <= 1;
     int64_t ld_off = nmine > 0 ? prob_offset(0) : 0;
-    int64_t ld_qoff = prob_offset(min(1, nmine - 1));
+    int64_t ld_qoff = nmine > 1 ? prob_offset(1) : 0;
 
     auto issue = [&](u32x4& dk, u32x4& dv, u32x4& dq) {
         const int row = tab[min(ld_b * BR + ld_row, L - 1)];
         const int64_t a = (int64_t)row * row_stride + ld_col;
-        dk = *reinterpret_cast<const u32x4*>(kp + ld_off + a);
-        dv = *reinterpret_cast<const u32x4*>(vp + ld_off + a);
-        if (QSTAGE) dq = *reinterpret_cast<const u32x4*>(qp + ld_qoff + a);
+        const int64_t akv = ld_dead ? 0 : ld_off + a;
+        dk = *reinterpret_cast<const u32x4*>(kp + akv);
+        dv = *reinterpret_cast<const u32x4*>(vp + akv);
+        if (QSTAGE) dq = *reinterpret_cast<const u32x4*>(qp + (q_dead ? 0 : ld_qoff + a));
         if (++ld_b == NB) {
             ld_b = 0;
-            if (ld_it + 1 < nmine) {
-                ++ld_it;
-                ld_off = ld_qoff;
-                ld_qoff = prob_offset(min(ld_it + 1, nmine - 1));
-            }
+            ++ld_it;
+            ld_dead = ld_it >= nmine;
+            q_dead = ld_it + 1 >= nmine;
+            ld_off = ld_qoff;
+            if (!q_dead) ld_qoff = prob_offset(ld_it + 1);
         }
     };
+
+    // swizzled position of this thread's V chunk (16-byte aligned) and whether
+    // its halves are stored swapped (done in registers)
+    const int v_put = v_chunk_offset<D>(ld_row, ld_col / 8);
+    const bool v_swap = v_halves_swapped<D>(ld_row);
 
     auto put = [&](const u32x4& dk, const u32x4& dv, const u32x4& dq, int buf, int blk) {
         if (stager) {
             *reinterpret_cast<u32x4*>(&kbuf[buf][ld_row * G::KSTR + ld_col]) = dk;
-            *reinterpret_cast<u32x4*>(&vbuf[buf][ld_row * G::VSTR + ld_col]) = dv;
+            *reinterpret_cast<u32x4*>(&vbuf[buf][v_put]) = v_swap ? u32x4{dv.z, dv.w, dv.x, dv.y} : dv;
             if (QSTAGE) *reinterpret_cast<u32x4*>(&qstage[(blk * BR + ld_row) * G::KSTR + ld_col]) = dq;
         }
     };
@@ -203,23 +205,25 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))
             s1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         const uint16_t* kb = kbuf[buf];
+        bf16x8 ka0[G::KS], ka1[G::KS];
 #pragma unroll
         for (int s = 0; s < G::KS; ++s) {
-            const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(&kb[li * G::KSTR + (4 * s + lg) * 8]);
-            const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(&kb[(16 + li) * G::KSTR + (4 * s + lg) * 8]);
+            ka0[s] = *reinterpret_cast<const bf16x8*>(&kb[li * G::KSTR + (4 * s + lg) * 8]);
+            ka1[s] = *reinterpret_cast<const bf16x8*>(&kb[(16 + li) * G::KSTR + (4 * s + lg) * 8]);
+        }
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
 #pragma unroll
             for (int t = 0; t < QT; ++t) {
-                if (wave * QT + t < ntiles) {
-                    s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qreg[t][s], s0[t], 0, 0, 0);
-                    s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qreg[t][s], s1[t], 0, 0, 0);
-                }
+                s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[s], qreg[t][s], s0[t], 0, 0, 0);
+                s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[s], qreg[t][s], s1[t], 0, 0, 0);
             }
         }
         const bool mask = ragged && blk == NB - 1;
         const int kbase = blk * BR + 4 * lg;
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
-            if (wave * QT + t < ntiles) {
+            {
                 if (mask) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -255,48 +259,47 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))
     // plus 4) so a lane's 4+4 accumulator rows are 8 consecutive d.
     auto v_step = [&](int buf) {
         uint16_t* vb = vbuf[buf];
-        // transposing fetch: lane (li, lg) addresses row 4*lg + li/4 (+16) at
-        // 4 consecutive d; it receives 4 consecutive keys of one d column
-        const int rlo = (4 * lg + (li >> 2)) * G::VSTR + 8 * (li & 3);
-        const int rhi = rlo + 16 * G::VSTR;
+        // transposing fetch: lane (li, lg) addresses row 4*lg + li/4 (and that
+        // +16) at 4 consecutive d (column 4*(dt/2) + li%4, half dt%2); it
+        // receives 4 consecutive keys of one d column
+        const int vr = v_fetch_row(li, lg);
+        bf16x8 va[G::DT];
 #pragma unroll
         for (int dt = 0; dt < G::DT; ++dt) {
-            const int col = 32 * (dt >> 1) + 4 * (dt & 1);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[rlo + col]));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[rhi + col]));
+            const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
             const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
-#pragma unroll
-            for (int t = 0; t < QT; ++t)
-                if (wave * QT + t < ntiles)
-                    oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pk[t], oacc[t][dt], 0, 0, 0);
+            va[dt] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
         }
 #pragma unroll
-        for (int t = 0; t < QT; ++t)
-            if (wave * QT + t < ntiles)
-                osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[t], osum[t], 0, 0, 0);
+        for (int t = 0; t < QT; ++t) {
+            osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[t], osum[t], 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt)
+                oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk[t], oacc[t][dt], 0, 0, 0);
+        }
     };
 
     // after the last block: normalise and store this wave's rows of the problem
     auto finish_problem = [&]() {
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
-            if (wave * QT + t < ntiles) {
-                const float inv = 1.0f / osum[t][0];
-                const int row = (wave * QT + t) * 16 + li;
-                if (row < L) {
-                    uint16_t* dst = op + cur_off + (int64_t)tab[row] * row_stride + 8 * lg;
+            // the row sum is >= 1 (the running maximum's own term), so the
+            // hardware reciprocal (1 ulp) is exact enough for a bf16 output
+            const float inv = __builtin_amdgcn_rcpf(osum[t][0]);
+            const int row = (wave * QT + t) * 16 + li;
+            if (row < L) {
+                uint16_t* dst = op + cur_off + (int64_t)tab[row] * row_stride + 8 * lg;
 #pragma unroll
-                    for (int p = 0; p < D / 32; ++p) {
-                        u32x4 w;
+                for (int p = 0; p < D / 32; ++p) {
+                    bf16x8 o;
 #pragma unroll
-                        for (int i = 0; i < 4; i += 2) {
-                            w[i / 2] = bf16_bits(oacc[t][2 * p][i] * inv) | (bf16_bits(oacc[t][2 * p][i + 1] * inv) << 16);
-                            w[2 + i / 2] =
-                                bf16_bits(oacc[t][2 * p + 1][i] * inv) | (bf16_bits(oacc[t][2 * p + 1][i + 1] * inv) << 16);
-                        }
-                        *reinterpret_cast<u32x4*>(dst + 32 * p) = w;
+                    for (int i = 0; i < 4; ++i) {
+                        o[i] = static_cast<__bf16>(oacc[t][2 * p][i] * inv);
+                        o[4 + i] = static_cast<__bf16>(oacc[t][2 * p + 1][i] * inv);
                     }
+                    *reinterpret_cast<bf16x8*>(dst + 32 * p) = o;
                 }
             }
         }
@@ -339,16 +342,33 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))
             issue(sk[u], sv[u], sq[u]);
             __syncthreads();
             if (live) {
-                k_step(u & 1, blk);
-                v_step(u & 1);
+                if (computes) {
+                    k_step(u & 1, blk);
+                    v_step(u & 1);
+                }
                 if (++blk == NB) {
-                    finish_problem();
+                    if (computes) finish_problem();
                     blk = 0;
                     ++c_it;
                 }
             }
         }
     }
+}
+
+// The two passes as distinct kernels (so profiles tell them apart).
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE>
+__global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_local_pass_bf16(
+    PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
+    float scale_log2) {
+    pass_body<D, QT, PD, LMAX, QSTAGE, false>(g, qp, kp, vp, op, scale_log2);
+}
+
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE>
+__global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_global_pass_bf16(
+    PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
+    float scale_log2) {
+    pass_body<D, QT, PD, LMAX, QSTAGE, true>(g, qp, kp, vp, op, scale_log2);
 }
 
 int grid_for(const void* kern, int threads, int nprob) {
@@ -385,7 +405,8 @@ int grid_for(const void* kern, int threads, int nprob) {
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE>
 hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o,
                       hipStream_t st) {
-    auto kfn = &pass_bf16_kernel<D, QT, MAXW, PD, WPE, LMAX, QSTAGE>;
+    auto kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE>
+                        : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE>;
     const void* kern = reinterpret_cast<const void*>(kfn);
     const int threads = 64 * waves;
     if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.L > LMAX || (g.L + 15) / 16 > QT * waves)

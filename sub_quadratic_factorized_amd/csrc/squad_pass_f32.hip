@@ -31,7 +31,7 @@ __global__ __launch_bounds__(64 * NWAVE) void pass_f32_kernel(PassGeom g, const 
     const int row_stride = g.heads * D;
 
     const ProblemIndex pr = decode_problem(g, blockIdx.x);
-    const int base = g.global ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
+    const int base = g.global ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);  // run-time pass selector
     const int64_t poff = ((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D;
 
     for (int r = tid; r < L; r += blockDim.x) tab[r] = g.global ? win_origin(g, r) : slot_offset(g, r);
