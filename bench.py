@@ -32,7 +32,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PAGES_MS_PER_BLOCK = 4.27      # the pages' SQuad attention latency per block (H100, bf16, n = 18,480)
 KERNEL_SOURCES = ["sub_quadratic_factorized_amd/csrc/squad_pass_bf16.hip",
-                  "sub_quadratic_factorized_amd/csrc/squad_internal.h"]
+                  "sub_quadratic_factorized_amd/csrc/squad_internal.h",
+                  "sub_quadratic_factorized_amd/csrc/squad_layout.h"]
+# rocprofv3 runs whose CSV output --summarize-profiles turns into the files under profiles/
+PROFILE_ARGS = "--no-cpu-baseline --steps 20 --warmup 2 --kernel-iters 20 --copy-calibration-mib 512"
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d <out>/trace -o run -- python3 bench.py " + PROFILE_ARGS,
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o run -- python3 bench.py " + PROFILE_ARGS,
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o run -- python3 bench.py " + PROFILE_ARGS,
+}
+PASS_KERNELS = {"squad_local_pass": "squad_local_pass_bf16", "squad_global_pass": "squad_global_pass_bf16"}
 
 
 def eprint(*a):
@@ -72,6 +81,111 @@ def traffic_from_profile(kernel: str, workload: str):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def short_kernel_name(name: str) -> str:
+    """Kernel name without return type, namespaces and parameter list (template arguments kept)."""
+    name = name.strip('"')
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # the parameter list is the first '(' outside template brackets
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not name.startswith("(anonymous", i):
+            cut = i
+            break
+    name = name[:cut]
+    base, _, targs = name.partition("<")
+    base = base.split("::")[-1]
+    return base + ("<" + targs if targs else "")
+
+
+def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload: str,
+                       trace_log: str | None = None) -> None:
+    """Write profiles/ summaries from the CSV output of the three PROFILE_COMMANDS runs.
+
+    Hardware counters are scaled by what they read for the plain 512 MiB
+    device copy the same runs make (its bytes are known), so FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) become HBM bytes per launch of each pass."""
+    import csv
+    from sub_quadratic_factorized_amd import workloads as wl
+    w = wl.WORKLOADS[workload]
+    esize = 2 if w.dtype == "bf16" else 4
+    pass_bytes = 4 * w.B * w.n * w.heads * w.d * esize
+    copy_bytes = 512 << 20
+
+    def counter_means(d, counter):
+        vals = {}
+        for row in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(short_kernel_name(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+    fetch, write = counter_means(fetch_dir, "FETCH_SIZE"), counter_means(write_dir, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if "copyBuffer" in k)
+    fetch_scale = copy_bytes / 1024 / fetch[copy_name][0]
+    write_scale = copy_bytes / 1024 / write[copy_name][0]
+
+    stats = []
+    for row in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))):
+        stats.append((short_kernel_name(row["Name"]), int(row["Calls"]), float(row["AverageNs"]) / 1e3,
+                      float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
+    title = (f"{w.name}: B={w.B}, grid {w.T}x{w.Hs}x{w.Ws} (n={w.n}), {w.heads} heads, d={w.d}, "
+             f"window {w.wt}x{w.wh}x{w.ww} (m={w.m}, N_w={w.n_windows}), {w.dtype}")
+    src_hash = kernel_source_hash()
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_squad_passes_{w.name}.md"), "w") as f:
+        f.write(f"# Kernel trace: SQuad-Attention passes, {title}\n\n")
+        f.write("Command (repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; <out> any "
+                "scratch folder; --workload omitted = this workload):\n\n")
+        f.write("```\n" + PROFILE_COMMANDS["trace"] + "\n```\n\n")
+        f.write(f"Kernel source hash (bench.py kernel_source_hash): {src_hash}\n\n")
+        f.write("| kernel | calls | average (us) | min (us) | max (us) |\n|---|---|---|---|---|\n")
+        for name, calls, avg, lo, hi in stats:
+            shown = name if len(name) <= 72 else name[:69] + "..."
+            f.write(f"| {shown} | {calls} | {avg:.1f} | {lo:.1f} | {hi:.1f} |\n")
+        if trace_log:
+            own = [ln.strip() for ln in open(trace_log) if ln.startswith("[bench] ") and " ms" in ln]
+            f.write("\nbench.py's own HIP-event timings in the same profiled process (stderr):\n\n```\n"
+                    + "\n".join(own) + "\n```\n")
+    lines = []
+    for kname, kernel in PASS_KERNELS.items():
+        fk = next(k for k in fetch if k.startswith(kernel))
+        wk = next(k for k in write if k.startswith(kernel))
+        rd = fetch[fk][0] * fetch_scale * 1024
+        wr = write[wk][0] * write_scale * 1024
+        avg_us = next(s[2] for s in stats if s[0].startswith(kernel))
+        rec = {
+            "kernel": kname, "instance": fk, "workload": w.name,
+            "fetch_size_kib_per_dispatch": fetch[fk][0], "write_size_kib_per_dispatch": write[wk][0],
+            "dispatches": [fetch[fk][1], write[wk][1]],
+            "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_scale": fetch_scale, "write_scale": write_scale},
+            "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+            "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": pass_bytes,
+            "kernel_source_hash": src_hash,
+            "commands": [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"]],
+        }
+        with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{w.name}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        lines.append(f"| {fk} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} | {pass_bytes / 1e6:.1f} | "
+                     f"{(rd + wr) / pass_bytes:.3f} | {avg_us:.1f} | {(rd + wr) / avg_us / 1e3:.0f} |")
+    with open(os.path.join(ROOT, "profiles", f"hbm_traffic_squad_passes_{w.name}.md"), "w") as f:
+        f.write(f"# HBM traffic per launch: SQuad-Attention passes, {title}\n\n")
+        f.write("Commands (two counter passes, each its own run; repository root, after "
+                "`cd /tmp && export TMPDIR=/tmp`):\n\n```\n" + PROFILE_COMMANDS["fetch"] + "\n"
+                + PROFILE_COMMANDS["write"] + "\n```\n\n")
+        f.write(f"Kernel source hash: {src_hash}\n\n")
+        f.write(f"Calibration: the same runs copy {copy_bytes >> 20} MiB device to device ({copy_name}); "
+                f"FETCH_SIZE reads {fetch[copy_name][0]:.0f} KiB and WRITE_SIZE {write[copy_name][0]:.0f} KiB "
+                f"for it, so the scale factors are {fetch_scale:.3f} (reads) and {write_scale:.3f} (writes).\n\n")
+        f.write("| kernel | HBM read (MB) | HBM write (MB) | total (MB) | algorithmic (MB) | ratio | "
+                "trace avg (us) | GB/s |\n|---|---|---|---|---|---|---|---|\n")
+        f.write("\n".join(lines) + "\n")
 
 
 def cpu_baseline(w, min_s=10.0, budget_s=25.0):
@@ -122,7 +236,15 @@ def main():
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling hardware byte counters)")
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summaries from rocprofv3 CSV output, then exit (no GPU needed)")
+    ap.add_argument("--trace-log", default=None, help="stderr of the profiled trace run (with --summarize-profiles)")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        from sub_quadratic_factorized_amd import workloads as wl
+        summarize_profiles(*args.summarize_profiles, args.workload or wl.HEADLINE, args.trace_log)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",

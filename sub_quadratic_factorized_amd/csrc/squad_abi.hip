@@ -117,6 +117,15 @@ hipError_t run_pass(const Problem& pr, bool global, const void* q, const void* k
     return launch_pass_f32(g, pr.d, q, k, vals, out, st);
 }
 
+// Both passes over all heads, in order, on the caller's stream; the second
+// pass reads the first pass's output from `out` and updates it in place.
+hipError_t run_two_passes(const Problem& pr, bool local_first, const void* q, const void* k, const void* v,
+                          void* out, hipStream_t st) {
+    hipError_t e = run_pass(pr, !local_first, q, k, v, out, st);
+    if (e == hipSuccess) e = run_pass(pr, local_first, q, k, out, out, st);
+    return e;
+}
+
 squad_status_t run(Kind kind, const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int Hs,
                    int Ws, int wt, int wh, int ww, int d, int dtype, hipStream_t st) {
     Problem pr;
@@ -126,12 +135,10 @@ squad_status_t run(Kind kind, const void* q, const void* k, const void* v, void*
     hipError_t e = hipSuccess;
     switch (kind) {
         case Kind::kFwd:
-            e = run_pass(pr, false, q, k, v, out, st);
-            if (e == hipSuccess) e = run_pass(pr, true, q, k, out, out, st);
+            e = run_two_passes(pr, true, q, k, v, out, st);
             break;
         case Kind::kReversed:
-            e = run_pass(pr, true, q, k, v, out, st);
-            if (e == hipSuccess) e = run_pass(pr, false, q, k, out, out, st);
+            e = run_two_passes(pr, false, q, k, v, out, st);
             break;
         case Kind::kLocal:
             e = run_pass(pr, false, q, k, v, out, st);

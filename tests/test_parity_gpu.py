@@ -236,3 +236,10 @@ def test_rejections_raise():
     with pytest.raises(bd.SquadError) as e:
         bd.squad_attn_fwd(q, q, q.clone(), (3, 4, 4), (3, 2, 2), out=q)
     assert e.value.status == bd.SQUAD_ERR_ALIAS
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("op", ["fwd", "reversed"])
+def test_many_heads_small_dim(dtype, op):
+    # 32 heads at d=64: 64 windows x 64 slots per head, row stride 2048
+    run_small((4, 32, 32, 4, 4, 4), dtype, op, heads=32, d=64)
