@@ -188,6 +188,57 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
         f.write("\n".join(lines) + "\n")
 
 
+# Backbones of the FLOP-conformance sweep: native latent grid (81 frames, T = 21)
+# and attention heads x head dim (Wan 2.2 5B at 704x1280; Wan 2.1 1.3B and 14B at
+# 480x832).
+SWEEP_BACKBONES = {"5B": ((22, 40), 24), "1.3B": ((30, 52), 12), "14B": ((30, 52), 40)}
+
+
+def sweep_grids(native, count=10, span=30.0):
+    """`count` grids at the native aspect ratio with T = 21 whose token counts
+    grow geometrically over `span` (from 1/6 to 5 times the native n)."""
+    Hs0, Ws0 = native
+    out = []
+    for i in range(count):
+        s = ((1.0 / 6.0) * span ** (i / (count - 1))) ** 0.5
+        out.append((21, max(2, round(Hs0 * s)), max(2, round(Ws0 * s))))
+    return out
+
+
+def run_sweep(iters: int) -> None:
+    """One JSON line per (backbone, grid): the window rule's window, the
+    closed-form FLOPs on the padded grid against the 8hd n^1.5 optimum, and the
+    measured time of squad_attn_fwd_padded (bf16, d = 128, synthetic inputs)."""
+    import torch
+    from sub_quadratic_factorized_amd import binding as bd
+    d = 128
+    for name, (native, heads) in SWEEP_BACKBONES.items():
+        for grid in sweep_grids(native):
+            T, Hs, Ws = grid
+            win = bd.squad_window_solve(grid)
+            n = T * Hs * Ws
+            flops = bd.squad_attn_flops_padded(1, heads, *grid, *win, d)
+            optimum = 8.0 * heads * d * n ** 1.5
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(n)  # seeded N(0, 1) drawn on the device: timing only, no parity here
+            q, k, v = (torch.randn((1, n, heads, d), generator=gen, device="cuda").to(torch.bfloat16)
+                       for _ in range(3))
+            need = bd.squad_attn_padded_workspace_bytes(1, heads, *grid, *win, d, bd.SQUAD_BF16)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            out = torch.empty_like(q)
+            ms = time_loop(lambda s: bd.squad_attn_fwd_padded(q, k, v, grid, win, out=out, workspace=ws),
+                           iters, [None])
+            _, Hp, Wp = (T, -(-Hs // win[1]) * win[1], -(-Ws // win[2]) * win[2])
+            rec = {"backbone": name, "heads": heads, "grid": list(grid), "n": n, "window": list(win),
+                   "padded_grid": [T, Hp, Wp], "closed_form_tflops": flops / 1e12,
+                   "over_optimum": flops / optimum - 1.0, "ms": ms, "tflops_per_s": flops / (ms * 1e-3) / 1e12,
+                   "algorithmic_gbs": bd.squad_attn_bytes_padded(1, heads, *grid, *win, d, bd.SQUAD_BF16)
+                   / (ms * 1e-3) / 1e9}
+            print(json.dumps(rec), flush=True)
+            del q, k, v, ws, out
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(w, min_s=10.0, budget_s=25.0):
     """The fp64 oracle on host cores over a bounded sample of the workload's heads."""
     import numpy as np
@@ -239,6 +290,8 @@ def main():
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summaries from rocprofv3 CSV output, then exit (no GPU needed)")
     ap.add_argument("--trace-log", default=None, help="stderr of the profiled trace run (with --summarize-profiles)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the window-rule sweep (10 grids x 3 backbones, padded entry point): one JSON line per grid")
     args = ap.parse_args()
 
     if args.summarize_profiles:
@@ -259,6 +312,10 @@ def main():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         sys.exit(1)
     bd.lib()  # fail loudly if the HIP library is missing
+
+    if args.sweep:
+        run_sweep(max(args.kernel_iters // 5, 5))
+        return
 
     w = wl.WORKLOADS[args.workload or wl.HEADLINE]
     grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)

@@ -29,7 +29,8 @@
  *
  * Ownership.  The caller allocates and owns every buffer.  The library keeps no
  * per-call state and allocates nothing; out doubles as the intermediate Y of
- * squad_attn_fwd, so no workspace is needed.  Prior contents of out are
+ * squad_attn_fwd, so no workspace is needed (the padded entry point takes one
+ * for the padded positions).  Prior contents of out are
  * ignored; they are undefined after a failed launch.
  *
  * Semantics.  Every compute entry point is asynchronous on `stream` (0 = the
@@ -74,7 +75,8 @@ typedef enum {
     SQUAD_ERR_UNSUPPORTED = 3,
     SQUAD_ERR_ALIAS = 4,
     SQUAD_ERR_ALIGN = 5,
-    SQUAD_ERR_HIP = 6
+    SQUAD_ERR_HIP = 6,
+    SQUAD_ERR_WORKSPACE = 7
 } squad_status_t;
 
 /* out = Attn_G(q, k, Attn_L(q, k, v)): the SQuad-Attention forward pass.
@@ -104,6 +106,81 @@ squad_status_t squad_attn_fwd_reversed(const void* q, const void* k, const void*
                                        int B, int heads, int T, int Hs, int Ws,
                                        int wt, int wh, int ww, int d,
                                        int dtype, hipStream_t stream);
+
+/* Grids a window does not tile (paperpeel full text, appendix paragraph
+ * "Conformance to the theoretical curves is quantitative": a window that does
+ * not divide the latent grid is made to fit by a little reflect padding).
+ *
+ * out = the real tokens of SQuad on the padded grid: the (T, Hs, Ws) grid is
+ * extended at the bottom and right to (T, Hp, Wp), Hp = ceil(Hs/wh)*wh and
+ * Wp = ceil(Ws/ww)*ww, each added position carrying the q, k and v of its
+ * mirror image about the last row or column (the edge is not repeated; padded
+ * position y >= Hs mirrors row 2*(Hs-1) - y, likewise x); both passes run over
+ * the padded grid, padded tokens being ordinary queries, keys and values, and
+ * only the outputs of the real tokens are written.  The time axis is never
+ * padded: T % wt must be 0.  Nothing is copied: the kernels address mirror
+ * images directly.
+ *
+ * q, k, v, out: [B, n, heads, d] as for squad_attn_fwd (n = T*Hs*Ws, the real
+ * grid).  workspace: device buffer of at least
+ * squad_attn_padded_workspace_bytes(...) bytes, 16-byte aligned, holding the
+ * local outputs of the padded positions between the two passes (contents on
+ * entry ignored, undefined afterwards; must not overlap q, k, v or out; one
+ * workspace must not be used by two calls that may run at the same time).
+ * When the window tiles the grid the call is squad_attn_fwd: the workspace is
+ * not used (it may be NULL) and out may be v.  Otherwise out must not overlap
+ * v either (mirror images read other windows' rows of v).
+ *
+ * Errors as squad_attn_fwd, except: SQUAD_ERR_SHAPE for T % wt != 0, wh > Hs
+ * or ww > Ws (instead of any non-tiling window), with the sizes taken on the
+ * padded grid; SQUAD_ERR_UNSUPPORTED also for a padded grid with T > 2047 or
+ * Hp or Wp > 1023; SQUAD_ERR_WORKSPACE (after the NULL checks) for a NULL or
+ * too small workspace when padding is needed. */
+squad_status_t squad_attn_fwd_padded(const void* q, const void* k, const void* v, void* out,
+                                     void* workspace, size_t workspace_bytes,
+                                     int B, int heads, int T, int Hs, int Ws,
+                                     int wt, int wh, int ww, int d,
+                                     int dtype, hipStream_t stream);
+
+/* Validation only for squad_attn_fwd_padded (pure host function). */
+squad_status_t squad_attn_check_padded(const void* q, const void* k, const void* v, const void* out,
+                                       const void* workspace, size_t workspace_bytes,
+                                       int B, int heads, int T, int Hs, int Ws,
+                                       int wt, int wh, int ww, int d, int dtype);
+
+/* Bytes of workspace squad_attn_fwd_padded needs: B * (padded positions per
+ * batch element) * heads * d * sizeof(dtype); 0 when the window tiles the grid
+ * or the problem is empty; -1 on a shape or dtype the padded entry point
+ * rejects.  Pure host function. */
+long long squad_attn_padded_workspace_bytes(int B, int heads, int T, int Hs, int Ws,
+                                            int wt, int wh, int ww, int d, int dtype);
+
+/* FLOPs of one squad_attn_fwd_padded call, counted as squad_attn_flops on the
+ * padded grid (the work done): 4*B*heads*d*n_p*(m + N_w), n_p = T*Hp*Wp,
+ * N_w = n_p/m.  -1 on a rejected shape.  Pure host function. */
+double squad_attn_flops_padded(int B, int heads, int T, int Hs, int Ws,
+                               int wt, int wh, int ww, int d);
+
+/* Algorithmic HBM bytes of one squad_attn_fwd_padded call: each pass reads
+ * three rows per padded-grid token-head, the local pass writes one per padded
+ * token-head and the global pass one per real token-head:
+ * (7*n_p + n)*B*heads*d*sizeof(dtype).  -1 on a rejected shape or dtype. */
+double squad_attn_bytes_padded(int B, int heads, int T, int Hs, int Ws,
+                               int wt, int wh, int ww, int d, int dtype);
+
+/* The window of the pages' FLOP-conformance sweep for a (T, Hs, Ws) grid
+ * (paperpeel full text, appendix paragraph "What is measured": the window
+ * spans the whole temporal extent, its spatial extents keep the grid's aspect
+ * ratio and its volume follows sqrt(n); integer extents, padding where it does
+ * not divide the grid).  Rule: wt = T; the continuous optimum
+ * wh*ww = sqrt(n)/T with wh:ww = Hs:Ws; wh and ww each rounded down or up
+ * (kept within 1..Hs and 1..Ws); of those windows the least closed-form cost
+ * 4hd(n_p*m + n_p^2/m) on the padded grid, ties to the aspect ratio nearer the
+ * grid's, then to the smaller window.  Gives 21x2x4 at 21x22x40 and at
+ * 21x30x52, as the pages state.  SQUAD_ERR_SHAPE for an extent < 1 or
+ * T*Hs*Ws >= 2^31; SQUAD_ERR_NULL for a NULL output pointer.  Pure host
+ * function. */
+squad_status_t squad_window_solve(int T, int Hs, int Ws, int* wt, int* wh, int* ww);
 
 /* Validation only: the status any compute entry point would return for these
  * arguments before launching (SQUAD_OK when it would launch).  Pure host
@@ -136,7 +213,8 @@ const char* squad_status_str(int status);
  * (0 if none). */
 int squad_attn_last_hip_error(void);
 
-/* Version of this ABI (bumped on any incompatible change). */
+/* Version of this ABI (bumped on any incompatible change; 2 adds the padded
+ * entry points and SQUAD_ERR_WORKSPACE). */
 int squad_attn_abi_version(void);
 
 #ifdef __cplusplus

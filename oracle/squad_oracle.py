@@ -224,3 +224,113 @@ def squad_flops(B, heads, T, Hs, Ws, wt, wh, ww, d):
 def full_attention_flops(B, heads, n, d):
     """FLOPs of one full softmax attention over n tokens, same counting rule."""
     return B * heads * 2 * 2 * n * n * d
+
+
+# ---------------------------------------------------------------------------
+# Window rule and reflect padding (grids a window does not tile)
+# ---------------------------------------------------------------------------
+#
+# SQuad paper appendix, "What is measured" and "Conformance to the theoretical
+# curves is quantitative": the window is chosen afresh for every latent grid so
+# that its volume m follows sqrt(n); it always spans the whole temporal extent
+# (wt = T) and its spatial extents keep the grid's aspect ratio; m must be a
+# whole number of tokens, and a window that does not divide the grid is made to
+# fit by a little reflect padding.  The pages print no formula beyond this.
+# Reading taken: the continuous optimum has wt = T, wh * ww = sqrt(n) / T and
+# wh : ww = Hs : Ws; each spatial extent is rounded down or up (kept within
+# 1..extent), and of those (at most four) windows the one with the least
+# closed-form cost 4hd(n_p m + n_p^2 / m) on its padded grid (n_p tokens) wins;
+# ties go to the aspect ratio closer to the grid's, then to the smaller window.
+# This recovers the trained 21 x 2 x 4 window at both native grids (21 x 22 x 40
+# and 21 x 30 x 52), as the pages state.
+
+def padded_extent(size, w):
+    """Smallest multiple of w that is >= size."""
+    return -(-size // w) * w
+
+
+def solve_window(T, Hs, Ws):
+    """(wt, wh, ww) for the grid (T, Hs, Ws) under the rule above."""
+    from fractions import Fraction
+    n = T * Hs * Ws
+    area = math.sqrt(n) / T
+    wh_c = math.sqrt(area * Hs / Ws)
+    ww_c = math.sqrt(area * Ws / Hs)
+    cands = set()
+    for wh in (math.floor(wh_c), math.ceil(wh_c)):
+        for ww in (math.floor(ww_c), math.ceil(ww_c)):
+            cands.add((min(max(wh, 1), Hs), min(max(ww, 1), Ws)))
+
+    def key(c):
+        wh, ww = c
+        m = T * wh * ww
+        n_p = T * padded_extent(Hs, wh) * padded_extent(Ws, ww)
+        cost = Fraction(n_p * m * m + n_p * n_p, m)       # n_p m + n_p^2 / m, exactly
+        a, b = wh * Ws, ww * Hs                            # wh/ww against Hs/Ws
+        aspect = Fraction(max(a, b), min(a, b))
+        return (cost, aspect, m, wh)
+
+    wh, ww = min(cands, key=key)
+    return T, wh, ww
+
+
+def reflect_index(i, size):
+    """Source index of position i of an axis of length `size` extended past its
+    end by mirroring about the last element (the edge is not repeated)."""
+    return i if i < size else 2 * (size - 1) - i
+
+
+def reflect_pad_tokens(x, T, Hs, Ws, Hp, Wp):
+    """[n, ...] in (t, y, x) order -> [T*Hp*Wp, ...]: the grid extended at the
+    bottom and right to (T, Hp, Wp) by mirroring (reading: padding at the far
+    end only; the time axis is never padded since wt = T)."""
+    if Hp - Hs > Hs - 1 or Wp - Ws > Ws - 1:
+        raise ValueError("reflect padding must be shorter than the axis")
+    g = np.asarray(x).reshape((T, Hs, Ws) + np.shape(x)[1:])
+    widths = [(0, 0), (0, Hp - Hs), (0, Wp - Ws)] + [(0, 0)] * (g.ndim - 3)
+    return np.pad(g, widths, mode="reflect").reshape((T * Hp * Wp,) + np.shape(x)[1:])
+
+
+def crop_tokens(x, T, Hp, Wp, Hs, Ws):
+    """Inverse of the padding's layout change: the (T, Hs, Ws) tokens of a
+    (T, Hp, Wp) token array, in (t, y, x) order."""
+    g = np.asarray(x).reshape((T, Hp, Wp) + np.shape(x)[1:])
+    return g[:, :Hs, :Ws].reshape((T * Hs * Ws,) + np.shape(x)[1:])
+
+
+def padded_grid(T, Hs, Ws, wt, wh, ww):
+    if T % wt:
+        raise ValueError("the window must span whole frames (T % wt == 0)")
+    return T, padded_extent(Hs, wh), padded_extent(Ws, ww)
+
+
+def squad_head_padded(q, k, v, grid, window):
+    """SQuad on a grid the window need not tile: reflect-pad Q, K and V, run
+    both passes on the padded grid (padded tokens are ordinary keys, values and
+    queries there), keep the outputs of the real tokens.  [n, d] -> [n, d]."""
+    T, Hs, Ws = grid
+    _, Hp, Wp = padded_grid(T, Hs, Ws, *window)
+    table = window_slot_table(T, Hp, Wp, *window)
+    qp, kp, vp = (reflect_pad_tokens(a, T, Hs, Ws, Hp, Wp) for a in (q, k, v))
+    return crop_tokens(squad_head(qp, kp, vp, table), T, Hp, Wp, Hs, Ws)
+
+
+def squad_attention_padded(q, k, v, geom):
+    """squad_attention for any window with wt | T; geom = (B, heads, T, Hs, Ws,
+    wt, wh, ww, d)."""
+    B, heads, T, Hs, Ws, wt, wh, ww, d = geom
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(q.shape, dtype=np.float64)
+    for b in range(B):
+        for h in range(heads):
+            out[b, :, h, :] = squad_head_padded(q[b, :, h, :], k[b, :, h, :], v[b, :, h, :],
+                                                (T, Hs, Ws), (wt, wh, ww))
+    return out
+
+
+def squad_flops_padded(B, heads, T, Hs, Ws, wt, wh, ww, d):
+    """FLOPs of the operator on the padded grid (the work actually done)."""
+    _, Hp, Wp = padded_grid(T, Hs, Ws, wt, wh, ww)
+    return squad_flops(B, heads, T, Hp, Wp, wt, wh, ww, d)

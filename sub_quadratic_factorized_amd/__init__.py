@@ -13,10 +13,15 @@ from .binding import (  # noqa: F401
     SquadError,
     squad_attn_bytes,
     squad_attn_flops,
+    squad_attn_bytes_padded,
+    squad_attn_flops_padded,
     squad_attn_fwd,
+    squad_attn_fwd_padded,
     squad_attn_fwd_reversed,
     squad_attn_global,
     squad_attn_local,
     squad_attn_max_len,
+    squad_attn_padded_workspace_bytes,
     squad_status_str,
+    squad_window_solve,
 )

@@ -27,9 +27,12 @@ SQUAD_ERR_UNSUPPORTED = 3
 SQUAD_ERR_ALIAS = 4
 SQUAD_ERR_ALIGN = 5
 SQUAD_ERR_HIP = 6
+SQUAD_ERR_WORKSPACE = 7
 
 COMPUTE_ENTRY_POINTS = ("squad_attn_fwd", "squad_attn_local", "squad_attn_global", "squad_attn_fwd_reversed")
 ALL_SYMBOLS = COMPUTE_ENTRY_POINTS + (
+    "squad_attn_fwd_padded", "squad_attn_check_padded", "squad_attn_padded_workspace_bytes",
+    "squad_attn_flops_padded", "squad_attn_bytes_padded", "squad_window_solve",
     "squad_attn_check", "squad_attn_max_len", "squad_attn_flops", "squad_attn_bytes", "squad_status_str",
     "squad_attn_last_hip_error", "squad_attn_abi_version",
 )
@@ -61,6 +64,19 @@ def lib() -> ctypes.CDLL:
         f.restype = i
     L.squad_attn_check.argtypes = [p, p, p, p] + [i] * 10
     L.squad_attn_check.restype = i
+    sz, ip = ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)
+    L.squad_attn_fwd_padded.argtypes = [p, p, p, p, p, sz] + [i] * 10 + [p]
+    L.squad_attn_fwd_padded.restype = i
+    L.squad_attn_check_padded.argtypes = [p, p, p, p, p, sz] + [i] * 10
+    L.squad_attn_check_padded.restype = i
+    L.squad_attn_padded_workspace_bytes.argtypes = [i] * 10
+    L.squad_attn_padded_workspace_bytes.restype = ctypes.c_longlong
+    L.squad_attn_flops_padded.argtypes = [i] * 9
+    L.squad_attn_flops_padded.restype = d
+    L.squad_attn_bytes_padded.argtypes = [i] * 10
+    L.squad_attn_bytes_padded.restype = d
+    L.squad_window_solve.argtypes = [i, i, i, ip, ip, ip]
+    L.squad_window_solve.restype = i
     L.squad_attn_max_len.argtypes = [i, i]
     L.squad_attn_max_len.restype = i
     L.squad_attn_flops.argtypes = [i] * 9
@@ -107,6 +123,32 @@ def squad_status_str(status: int) -> str:
     return status_str(status)
 
 
+def squad_window_solve(grid) -> tuple:
+    """(wt, wh, ww) the window rule picks for the latent grid (T, Hs, Ws)."""
+    out = [ctypes.c_int(0) for _ in range(3)]
+    st = lib().squad_window_solve(*grid, *(ctypes.byref(o) for o in out))
+    if st != SQUAD_OK:
+        raise SquadError(st, "squad_window_solve")
+    return tuple(o.value for o in out)
+
+
+def squad_attn_padded_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> int:
+    return lib().squad_attn_padded_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_attn_flops_padded(B, heads, T, Hs, Ws, wt, wh, ww, d) -> float:
+    return lib().squad_attn_flops_padded(B, heads, T, Hs, Ws, wt, wh, ww, d)
+
+
+def squad_attn_bytes_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> float:
+    return lib().squad_attn_bytes_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_attn_check_padded(q, k, v, out, ws, ws_bytes, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> int:
+    """Host-only validation status of squad_attn_fwd_padded for raw pointers."""
+    return lib().squad_attn_check_padded(q, k, v, out, ws, ws_bytes, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
 # ---------------------------------------------------------------------------
 # torch tensor entry points
 # ---------------------------------------------------------------------------
@@ -120,7 +162,7 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
 
 
-def _call(name, q, k, v, out, grid, window, stream):
+def _check_tensors(q, k, v, out, grid):
     import torch
     for t in (q, k, v):
         if t.dim() != 4 or not t.is_contiguous() or t.device.type != "cuda":
@@ -131,11 +173,18 @@ def _call(name, q, k, v, out, grid, window, stream):
         out = torch.empty_like(q)
     elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
+    T, Hs, Ws = grid
+    if T * Hs * Ws != q.shape[1]:
+        raise ValueError(f"grid {tuple(grid)} has {T * Hs * Ws} tokens, tensors have n = {q.shape[1]}")
+    return out
+
+
+def _call(name, q, k, v, out, grid, window, stream):
+    import torch
+    out = _check_tensors(q, k, v, out, grid)
     B, n, heads, d = q.shape
     T, Hs, Ws = grid
     wt, wh, ww = window
-    if T * Hs * Ws != n:
-        raise ValueError(f"grid {tuple(grid)} has {T * Hs * Ws} tokens, tensors have n = {n}")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
@@ -164,3 +213,33 @@ def squad_attn_global(q, k, v, grid, window, out=None, stream=None):
 def squad_attn_fwd_reversed(q, k, v, grid, window, out=None, stream=None):
     """out = Attn_L(q, k, Attn_G(q, k, v)): the reverse order."""
     return _call("squad_attn_fwd_reversed", q, k, v, out, grid, window, stream)
+
+
+def squad_attn_fwd_padded(q, k, v, grid, window, out=None, workspace=None, stream=None):
+    """SQuad on a grid the window need not tile (reflect padding at the bottom
+    and right, outputs of the real tokens only).  `workspace` is a device
+    tensor of at least squad_attn_padded_workspace_bytes bytes; if None one is
+    allocated through torch for this call."""
+    import torch
+    out = _check_tensors(q, k, v, out, grid)
+    B, n, heads, d = q.shape
+    T, Hs, Ws = grid
+    wt, wh, ww = window
+    dt = _dtype_code(q)
+    need = squad_attn_padded_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dt)
+    if need < 0:
+        raise SquadError(SQUAD_ERR_SHAPE, "squad_attn_fwd_padded")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().squad_attn_fwd_padded(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         workspace.data_ptr(), ws_bytes, B, heads, T, Hs, Ws, wt, wh, ww, d, dt,
+                                         stream)
+    if st != SQUAD_OK:
+        raise SquadError(st, "squad_attn_fwd_padded")
+    return out

@@ -4,6 +4,7 @@
 #include "squad_attn.h"
 #include "squad_internal.h"
 
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -20,6 +21,12 @@ struct Problem {
     int64_t n, m, nw;
     int64_t elems;  // B*n*heads*d
     size_t bytes;   // elems * sizeof(dtype)
+    // padded grids: extents the window tiles, tokens per batch element of the
+    // padded grid, and of the side buffer (padded positions only); N_w above
+    // then counts the windows of the padded grid
+    int Hp = 0, Wp = 0;
+    int64_t np = 0, npad = 0;
+    size_t ws_bytes = 0;  // B*npad*heads*d*sizeof(dtype)
 };
 
 int esize(int dtype) { return dtype == SQUAD_BF16 ? 2 : 4; }
@@ -63,6 +70,50 @@ squad_status_t check_shape(int B, int heads, int T, int Hs, int Ws, int wt, int 
     return SQUAD_OK;
 }
 
+// Shape checks of the padded entry points: the window must span whole frames
+// (T % wt == 0) and be no larger than the grid spatially (mirror padding is
+// shorter than the axis it extends); the grid is extended at the bottom and
+// right to multiples of wh and ww.  Same outcomes as check_shape otherwise.
+squad_status_t check_shape_padded(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d,
+                                  Problem* pr, bool* empty) {
+    *empty = false;
+    if (B < 0 || heads < 0) return SQUAD_ERR_SHAPE;
+    if (T < 1 || Hs < 1 || Ws < 1 || wt < 1 || wh < 1 || ww < 1 || d < 1) return SQUAD_ERR_SHAPE;
+    if (T % wt != 0 || wh > Hs || ww > Ws) return SQUAD_ERR_SHAPE;
+    const int64_t Hp = ((int64_t)Hs + wh - 1) / wh * wh, Wp = ((int64_t)Ws + ww - 1) / ww * ww;
+    const int64_t np = (int64_t)T * Hp * Wp;
+    if (np >= ((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;
+    const int64_t n = (int64_t)T * Hs * Ws;
+    const int64_t m = (int64_t)wt * wh * ww;
+    pr->B = B;
+    pr->heads = heads;
+    pr->T = T;
+    pr->Hs = Hs;
+    pr->Ws = Ws;
+    pr->wt = wt;
+    pr->wh = wh;
+    pr->ww = ww;
+    pr->d = d;
+    pr->n = n;
+    pr->m = m;
+    pr->nw = np / m;
+    pr->Hp = (int)Hp;
+    pr->Wp = (int)Wp;
+    pr->np = np;
+    pr->npad = np - n;
+    if (B == 0 || heads == 0) {
+        *empty = true;
+        pr->elems = 0;
+        return SQUAD_OK;
+    }
+    const long double el = (long double)B * (long double)np * (long double)heads * (long double)d;
+    if (el >= (long double)((int64_t)1 << 62)) return SQUAD_ERR_SHAPE;
+    pr->elems = (int64_t)B * n * heads * d;
+    const long double probs = (long double)B * heads * (long double)(m > pr->nw ? m : pr->nw);
+    if (probs >= (long double)((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;
+    return SQUAD_OK;
+}
+
 bool overlaps(const void* a, const void* b, size_t bytes) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + bytes && y < x + bytes;
@@ -86,7 +137,46 @@ squad_status_t validate(const void* q, const void* k, const void* v, const void*
     return SQUAD_OK;
 }
 
+// Arguments of the padded entry points: the checks of validate() in the same
+// order, plus the side buffer (SQUAD_ERR_WORKSPACE after the NULL checks).
+// When the window tiles the grid nothing is padded, the workspace is ignored
+// and out == v stays allowed; otherwise out must not overlap v at all (the
+// mirror images of a window's padded rows are other windows' rows of v).
+squad_status_t validate_padded(const void* q, const void* k, const void* v, const void* out, const void* ws,
+                               size_t ws_size, int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww,
+                               int d, int dtype, Problem* pr, bool* empty) {
+    squad_status_t s = check_shape_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, pr, empty);
+    if (s != SQUAD_OK) return s;
+    if (*empty) return SQUAD_OK;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return SQUAD_ERR_UNSUPPORTED;
+    const int maxlen = squad_attn_max_len(d, dtype);
+    if (maxlen == 0) return SQUAD_ERR_UNSUPPORTED;
+    if (pr->m > maxlen || pr->nw > maxlen) return SQUAD_ERR_UNSUPPORTED;
+    const bool padded = pr->npad > 0;
+    if (padded && (T > kMaxPaddedT || pr->Hp > kMaxPaddedHW || pr->Wp > kMaxPaddedHW)) return SQUAD_ERR_UNSUPPORTED;
+    pr->dtype = dtype;
+    if (!q || !k || !v || !out) return SQUAD_ERR_NULL;
+    pr->ws_bytes = (size_t)pr->B * (size_t)pr->npad * (size_t)pr->heads * (size_t)d * (size_t)esize(dtype);
+    if (padded && (!ws || ws_size < pr->ws_bytes)) return SQUAD_ERR_WORKSPACE;
+    uintptr_t bits = ((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)out);
+    if (padded) bits |= (uintptr_t)ws;
+    if (bits & 15u) return SQUAD_ERR_ALIGN;
+    pr->bytes = (size_t)pr->elems * (size_t)esize(dtype);
+    if (overlaps(out, q, pr->bytes) || overlaps(out, k, pr->bytes)) return SQUAD_ERR_ALIAS;
+    if ((padded || out != v) && overlaps(out, v, pr->bytes)) return SQUAD_ERR_ALIAS;
+    if (padded) {
+        const uintptr_t w = (uintptr_t)ws, e = w + pr->ws_bytes;
+        for (const void* t : {q, k, v, out}) {
+            const uintptr_t a = (uintptr_t)t;
+            if (a < e && w < a + pr->bytes) return SQUAD_ERR_ALIAS;
+        }
+    }
+    return SQUAD_OK;
+}
+
 PassGeom make_geom(const Problem& pr, bool global) {
+    const bool padded = pr.npad > 0;
+    const int Hp = padded ? pr.Hp : pr.Hs, Wp = padded ? pr.Wp : pr.Ws;
     PassGeom g;
     g.n = pr.n;
     g.heads = pr.heads;
@@ -98,8 +188,13 @@ PassGeom make_geom(const Problem& pr, bool global) {
     g.wt = pr.wt;
     g.wh = pr.wh;
     g.ww = pr.ww;
-    g.Cy = pr.Hs / pr.wh;
-    g.Cx = pr.Ws / pr.ww;
+    g.Cy = Hp / pr.wh;
+    g.Cx = Wp / pr.ww;
+    g.pad = padded ? 1 : 0;
+    g.Hp = Hp;
+    g.Wp = Wp;
+    g.pad_per_frame = pr.Hs * (Wp - pr.Ws) + (Hp - pr.Hs) * Wp;
+    g.npad = padded ? pr.npad : 0;
     g.global = global ? 1 : 0;
     g.div_heads = make_fastdiv((uint32_t)g.heads);
     g.div_P = make_fastdiv((uint32_t)g.P);
@@ -111,19 +206,77 @@ PassGeom make_geom(const Problem& pr, bool global) {
 }
 
 hipError_t run_pass(const Problem& pr, bool global, const void* q, const void* k, const void* vals, void* out,
-                    hipStream_t st) {
+                    void* ypad, hipStream_t st) {
     const PassGeom g = make_geom(pr, global);
-    if (pr.dtype == SQUAD_BF16) return launch_pass_bf16(g, pr.d, q, k, vals, out, st);
-    return launch_pass_f32(g, pr.d, q, k, vals, out, st);
+    if (pr.dtype == SQUAD_BF16) return launch_pass_bf16(g, pr.d, q, k, vals, out, ypad, st);
+    return launch_pass_f32(g, pr.d, q, k, vals, out, ypad, st);
 }
 
 // Both passes over all heads, in order, on the caller's stream; the second
-// pass reads the first pass's output from `out` and updates it in place.
+// pass reads the first pass's output from `out` (and, on a padded grid, from
+// the side buffer ypad) and updates `out` in place.
 hipError_t run_two_passes(const Problem& pr, bool local_first, const void* q, const void* k, const void* v,
-                          void* out, hipStream_t st) {
-    hipError_t e = run_pass(pr, !local_first, q, k, v, out, st);
-    if (e == hipSuccess) e = run_pass(pr, local_first, q, k, out, out, st);
+                          void* out, void* ypad, hipStream_t st) {
+    hipError_t e = run_pass(pr, !local_first, q, k, v, out, ypad, st);
+    if (e == hipSuccess) e = run_pass(pr, local_first, q, k, out, out, ypad, st);
     return e;
+}
+
+squad_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return SQUAD_OK;
+    g_last_hip_error = (int)e;
+    return SQUAD_ERR_HIP;
+}
+
+// The window rule: wt = T, the continuous optimum wh*ww = sqrt(n)/T with
+// wh : ww = Hs : Ws, each spatial extent rounded down or up (within
+// 1..extent), and of those windows the least 4hd(n_p m + n_p^2/m) on the
+// padded grid (n_p tokens); ties to the aspect ratio closer to the grid's, then
+// to the smaller m, then the smaller wh.  Costs compare exactly as fractions.
+void solve_window(int T, int Hs, int Ws, int* out_wh, int* out_ww) {
+    typedef unsigned __int128 u128;
+    const double n = (double)T * (double)Hs * (double)Ws;
+    const double area = sqrt(n) / T;
+    const double whc = sqrt(area * Hs / Ws), wwc = sqrt(area * Ws / Hs);
+    const int whs[2] = {(int)floor(whc), (int)ceil(whc)}, wws[2] = {(int)floor(wwc), (int)ceil(wwc)};
+    bool have = false;
+    u128 best_num = 0, best_den = 1, best_amax = 0, best_amin = 1;
+    int64_t best_m = 0;
+    int best_wh = 1, best_ww = 1;
+    for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < 2; ++b) {
+            const int wh = whs[a] < 1 ? 1 : (whs[a] > Hs ? Hs : whs[a]);
+            const int ww = wws[b] < 1 ? 1 : (wws[b] > Ws ? Ws : wws[b]);
+            const u128 m = (u128)T * wh * ww;
+            const u128 np = (u128)T * (u128)((Hs + wh - 1) / wh * wh) * (u128)((Ws + ww - 1) / ww * ww);
+            const u128 num = np * m * m + np * np, den = m;  // n_p m + n_p^2 / m
+            const u128 x = (u128)wh * Ws, y = (u128)ww * Hs;
+            const u128 amax = x > y ? x : y, amin = x > y ? y : x;
+            bool better = !have;
+            if (have) {
+                const u128 l = num * best_den, r = best_num * den;
+                if (l != r) {
+                    better = l < r;
+                } else {
+                    const u128 al = amax * best_amin, ar = best_amax * amin;
+                    if (al != ar) better = al < ar;
+                    else if ((int64_t)m != best_m) better = (int64_t)m < best_m;
+                    else better = wh < best_wh;
+                }
+            }
+            if (better) {
+                have = true;
+                best_num = num;
+                best_den = den;
+                best_amax = amax;
+                best_amin = amin;
+                best_m = (int64_t)m;
+                best_wh = wh;
+                best_ww = ww;
+            }
+        }
+    *out_wh = best_wh;
+    *out_ww = best_ww;
 }
 
 squad_status_t run(Kind kind, const void* q, const void* k, const void* v, void* out, int B, int heads, int T, int Hs,
@@ -135,23 +288,19 @@ squad_status_t run(Kind kind, const void* q, const void* k, const void* v, void*
     hipError_t e = hipSuccess;
     switch (kind) {
         case Kind::kFwd:
-            e = run_two_passes(pr, true, q, k, v, out, st);
+            e = run_two_passes(pr, true, q, k, v, out, nullptr, st);
             break;
         case Kind::kReversed:
-            e = run_two_passes(pr, false, q, k, v, out, st);
+            e = run_two_passes(pr, false, q, k, v, out, nullptr, st);
             break;
         case Kind::kLocal:
-            e = run_pass(pr, false, q, k, v, out, st);
+            e = run_pass(pr, false, q, k, v, out, nullptr, st);
             break;
         case Kind::kGlobal:
-            e = run_pass(pr, true, q, k, v, out, st);
+            e = run_pass(pr, true, q, k, v, out, nullptr, st);
             break;
     }
-    if (e != hipSuccess) {
-        g_last_hip_error = (int)e;
-        return SQUAD_ERR_HIP;
-    }
-    return SQUAD_OK;
+    return hip_status(e);
 }
 
 }  // namespace
@@ -190,6 +339,66 @@ squad_status_t squad_attn_fwd_reversed(const void* q, const void* k, const void*
                                        int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype,
                                        hipStream_t stream) {
     return squad::run(squad::Kind::kReversed, q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, stream);
+}
+
+squad_status_t squad_attn_fwd_padded(const void* q, const void* k, const void* v, void* out, void* workspace,
+                                     size_t workspace_bytes, int B, int heads, int T, int Hs, int Ws, int wt, int wh,
+                                     int ww, int d, int dtype, hipStream_t stream) {
+    squad::Problem pr;
+    bool empty = false;
+    const squad_status_t s = squad::validate_padded(q, k, v, out, workspace, workspace_bytes, B, heads, T, Hs, Ws,
+                                                    wt, wh, ww, d, dtype, &pr, &empty);
+    if (s != SQUAD_OK || empty) return s;
+    return squad::hip_status(
+        squad::run_two_passes(pr, true, q, k, v, out, pr.npad > 0 ? workspace : nullptr, stream));
+}
+
+squad_status_t squad_attn_check_padded(const void* q, const void* k, const void* v, const void* out,
+                                       const void* workspace, size_t workspace_bytes, int B, int heads, int T, int Hs,
+                                       int Ws, int wt, int wh, int ww, int d, int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    return squad::validate_padded(q, k, v, out, workspace, workspace_bytes, B, heads, T, Hs, Ws, wt, wh, ww, d,
+                                  dtype, &pr, &empty);
+}
+
+long long squad_attn_padded_workspace_bytes(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d,
+                                            int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return -1;
+    if (squad::check_shape_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1;
+    if (empty) return 0;
+    const long double bytes = (long double)B * pr.npad * heads * d * squad::esize(dtype);
+    if (bytes >= 9.0e18L) return -1;
+    return (long long)bytes;
+}
+
+double squad_attn_flops_padded(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d) {
+    squad::Problem pr;
+    bool empty = false;
+    if (squad::check_shape_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1.0;
+    if (empty) return 0.0;
+    return 4.0 * (double)B * heads * (double)d * (double)pr.np * (double)(pr.m + pr.nw);
+}
+
+double squad_attn_bytes_padded(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return -1.0;
+    if (squad::check_shape_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1.0;
+    if (empty) return 0.0;
+    const double row = (double)B * heads * d * squad::esize(dtype);
+    return row * (7.0 * (double)pr.np + (double)pr.n);
+}
+
+squad_status_t squad_window_solve(int T, int Hs, int Ws, int* wt, int* wh, int* ww) {
+    if (T < 1 || Hs < 1 || Ws < 1) return SQUAD_ERR_SHAPE;
+    if ((int64_t)T * Hs * Ws >= ((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;
+    if (!wt || !wh || !ww) return SQUAD_ERR_NULL;
+    squad::solve_window(T, Hs, Ws, wh, ww);
+    *wt = T;
+    return SQUAD_OK;
 }
 
 squad_status_t squad_attn_check(const void* q, const void* k, const void* v, const void* out, int B, int heads,
@@ -231,12 +440,13 @@ const char* squad_status_str(int status) {
         case SQUAD_ERR_ALIAS: return "output overlaps an input (only out == v is allowed)";
         case SQUAD_ERR_ALIGN: return "pointer not 16-byte aligned";
         case SQUAD_ERR_HIP: return "HIP runtime or launch error";
+        case SQUAD_ERR_WORKSPACE: return "workspace missing or smaller than squad_attn_padded_workspace_bytes";
         default: return "unknown status";
     }
 }
 
 int squad_attn_last_hip_error(void) { return squad::g_last_hip_error; }
 
-int squad_attn_abi_version(void) { return 1; }
+int squad_attn_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -49,15 +49,72 @@ struct PassGeom {
     int L;          // rows per problem (m local, N_w global)
     int P;          // problems per (b, h) (N_w local, m global)
     int nprob;      // B*heads*P
-    int Hs, Ws;     // grid extents (T is implied)
+    int Hs, Ws;     // grid extents (T is implied); the real grid when pad = 1
     int wt, wh, ww; // window extents
-    int Cy, Cx;     // windows along y and x
+    int Cy, Cx;     // windows along y and x (of the padded grid when pad = 1)
     int global;     // 0: local pass, 1: global pass
     // divisors of the problem decode and of the row maps
     FastDiv div_heads, div_P;         // problem -> (b, pi, h)
     FastDiv div_wins_t, div_Cx;       // window c -> (ct, cy, cx): Cy*Cx, Cx
     FastDiv div_slots_t, div_ww;      // slot j -> (jt, jy, jx): wh*ww, ww
+    // Padded grids (pad = 1).  The window tiles the grid (T, Hp, Wp) that
+    // extends (T, Hs, Ws) at the bottom and right by mirror images; windows,
+    // slots, Cy and Cx then refer to the padded grid, and a row is named by its
+    // packed padded coordinates (see pack_coords) instead of a token offset.
+    // The local outputs of padded tokens live in a side buffer of npad tokens
+    // per batch element ([B, npad, heads, d]).
+    int pad;
+    int Hp, Wp;
+    int pad_per_frame;  // Hs*(Wp - Ws) + (Hp - Hs)*Wp padded tokens per frame
+    int64_t npad;       // T * pad_per_frame
 };
+
+// Packed (t, y, x) of the padded grid: 11 bits of t, 10 of y and of x.  The
+// fields of a window origin and of an in-window offset add without carries,
+// so a row's coordinates are one integer addition away from its problem's.
+constexpr int kMaxPaddedT = 2047;
+constexpr int kMaxPaddedHW = 1023;
+
+__host__ __device__ inline int pack_coords(int t, int y, int x) { return (t << 20) | (y << 10) | x; }
+
+// Packed origin of window c of the padded grid.
+__host__ __device__ inline int win_coords(const PassGeom& g, int c) {
+    const int ct = (int)fdiv((uint32_t)c, g.div_wins_t);
+    const int r = c - ct * (int)g.div_wins_t.d;
+    const int cy = (int)fdiv((uint32_t)r, g.div_Cx);
+    const int cx = r - cy * g.Cx;
+    return pack_coords(ct * g.wt, cy * g.wh, cx * g.ww);
+}
+
+// Packed in-window offset of slot j.
+__host__ __device__ inline int slot_coords(const PassGeom& g, int j) {
+    const int jt = (int)fdiv((uint32_t)j, g.div_slots_t);
+    const int r = j - jt * (int)g.div_slots_t.d;
+    const int jy = (int)fdiv((uint32_t)r, g.div_ww);
+    return pack_coords(jt, jy, r - jy * g.ww);
+}
+
+// Position i of an axis of length size extended past its end by mirroring
+// about the last element (the edge itself is not repeated).
+__host__ __device__ inline int mirror(int i, int size) { return i < size ? i : 2 * (size - 1) - i; }
+
+// Token of the real grid whose values a padded position carries.
+__host__ __device__ inline int mirrored_token(const PassGeom& g, int p) {
+    const int t = p >> 20, y = (p >> 10) & 1023, x = p & 1023;
+    return (t * g.Hs + mirror(y, g.Hs)) * g.Ws + mirror(x, g.Ws);
+}
+
+__host__ __device__ inline bool is_real(const PassGeom& g, int p) {
+    return ((p >> 10) & 1023) < g.Hs && (p & 1023) < g.Ws;
+}
+
+// Index of a padded (not real) position in the side buffer: frame-major;
+// within a frame first the right margin of the real rows, then the bottom rows.
+__host__ __device__ inline int pad_index(const PassGeom& g, int p) {
+    const int t = p >> 20, y = (p >> 10) & 1023, x = p & 1023;
+    const int within = y < g.Hs ? y * (g.Wp - g.Ws) + (x - g.Ws) : g.Hs * (g.Wp - g.Ws) + (y - g.Hs) * g.Wp + x;
+    return t * g.pad_per_frame + within;
+}
 
 // Token index of slot 0 of window c (windows numbered row-major over their
 // tile coordinates (ct, cy, cx)).
@@ -95,10 +152,13 @@ __host__ __device__ inline ProblemIndex decode_problem(const PassGeom& g, int p)
 // launch status.  `vals` may equal `out` (in-place update, race-free because
 // every workgroup reads all rows of its problems before writing them, and the
 // problems of a pass partition the rows).
+// `ypad` is the side buffer of padded grids (unused when g.pad == 0): the
+// local pass writes the outputs of padded rows there, the global pass reads
+// its values for padded rows from it and stores real rows only.
 hipError_t launch_pass_bf16(const PassGeom& g, int d, const void* q, const void* k,
-                            const void* vals, void* out, hipStream_t stream);
+                            const void* vals, void* out, void* ypad, hipStream_t stream);
 hipError_t launch_pass_f32(const PassGeom& g, int d, const void* q, const void* k,
-                           const void* vals, void* out, hipStream_t stream);
+                           const void* vals, void* out, void* ypad, hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();

@@ -66,11 +66,13 @@ __device__ __forceinline__ float row_max4(float x) {
 // stream Q through the LDS stage (else each wave loads its Q tiles straight
 // into registers at a problem's first step, for problems too long to stage).
 // GP: the global pass (rows of a problem are windows at one slot) rather than
-// the local pass (rows are the slots of one window).
-template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP>
+// the local pass (rows are the slots of one window).  PAD: a padded grid (rows
+// named by packed padded coordinates; q, k and the local pass's values read
+// through mirror images; padded rows of Y in the side buffer yp).
+template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD>
 __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __restrict__ qp,
                                           const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
-                                          float scale_log2) {
+                                          uint16_t* yp, float scale_log2) {
     using G = Geo<D>;
     static_assert(PD % 2 == 0, "the LDS buffer of a step must be known at compile time");
     constexpr int QROWS = QSTAGE ? (LMAX + BR - 1) / BR * BR : 1;
@@ -101,14 +103,31 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     const int ld_col = (ch % G::KC) * 8;
 
     // row r of any problem of this pass sits at a fixed token offset from the
-    // problem's base token
-    for (int r = tid; r < L; r += blockDim.x) tab[r] = GP ? win_origin(g, r) : slot_offset(g, r);
+    // problem's base token (padded grids: at fixed packed coordinates)
+    for (int r = tid; r < L; r += blockDim.x)
+        tab[r] = PAD ? (GP ? win_coords(g, r) : slot_coords(g, r)) : (GP ? win_origin(g, r) : slot_offset(g, r));
     __syncthreads();
 
-    auto prob_offset = [&](int it) -> int64_t {
+    // A problem: unpadded, the offset of its base token's row (row r adds
+    // tab[r] * row_stride); padded, the (b, h) offsets into the tensors and
+    // into the side buffer, and its packed base coordinates.
+    struct Prob {
+        int64_t off, yoff;
+        int base;
+    };
+    auto problem = [&](int it) -> Prob {
         const ProblemIndex pr = decode_problem(g, (int)blockIdx.x + it * (int)gridDim.x);
+        if (PAD)
+            return Prob{(int64_t)pr.b * g.n * row_stride + (int64_t)pr.h * D,
+                        (int64_t)pr.b * g.npad * row_stride + (int64_t)pr.h * D,
+                        GP ? slot_coords(g, pr.pi) : win_coords(g, pr.pi)};
         const int base = GP ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
-        return ((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D;
+        return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0};
+    };
+    // offset, in q, k and the local pass's values, of the row with table entry tv
+    auto src_off = [&](const Prob& pr, int tv) -> int64_t {
+        if (PAD) return pr.off + (int64_t)mirrored_token(g, pr.base + tv) * row_stride;
+        return pr.off + (int64_t)tv * row_stride;
     };
 
     // ---- loader -------------------------------------------------------------
@@ -122,23 +141,30 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // all read the first 16 bytes of the tensor (one cached line, never used)
     bool ld_dead = nmine <= 0;
     bool q_dead = nmine <= 1;
-    int64_t ld_off = nmine > 0 ? prob_offset(0) : 0;
-    int64_t ld_qoff = nmine > 1 ? prob_offset(1) : 0;
+    Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0};
+    Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0};
 
     auto issue = [&](u32x4& dk, u32x4& dv, u32x4& dq) {
-        const int row = tab[min(ld_b * BR + ld_row, L - 1)];
-        const int64_t a = (int64_t)row * row_stride + ld_col;
-        const int64_t akv = ld_dead ? 0 : ld_off + a;
-        dk = *reinterpret_cast<const u32x4*>(kp + akv);
-        dv = *reinterpret_cast<const u32x4*>(vp + akv);
-        if (QSTAGE) dq = *reinterpret_cast<const u32x4*>(qp + (q_dead ? 0 : ld_qoff + a));
+        const int tv = tab[min(ld_b * BR + ld_row, L - 1)];
+        const int64_t a = src_off(ld_p, tv) + ld_col;
+        // the global pass's values are the local outputs: on a padded grid a
+        // padded row's come from the side buffer
+        const uint16_t* vb = vp;
+        int64_t av = a;
+        if (PAD && GP && !is_real(g, ld_p.base + tv)) {
+            vb = yp;
+            av = ld_p.yoff + (int64_t)pad_index(g, ld_p.base + tv) * row_stride + ld_col;
+        }
+        dk = *reinterpret_cast<const u32x4*>(kp + (ld_dead ? 0 : a));
+        dv = *reinterpret_cast<const u32x4*>(vb + (ld_dead ? 0 : av));
+        if (QSTAGE) dq = *reinterpret_cast<const u32x4*>(qp + (q_dead ? 0 : src_off(ld_q, tv) + ld_col));
         if (++ld_b == NB) {
             ld_b = 0;
             ++ld_it;
             ld_dead = ld_it >= nmine;
             q_dead = ld_it + 1 >= nmine;
-            ld_off = ld_qoff;
-            if (!q_dead) ld_qoff = prob_offset(ld_it + 1);
+            ld_p = ld_q;
+            if (!q_dead) ld_q = problem(ld_it + 1);
         }
     };
 
@@ -161,7 +187,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     f32x4 osum[QT];  // every row: running sum of P for the lane's query
     bf16x8 pk[QT];
     float mrun[QT];
-    int64_t cur_off = 0;
+    Prob cur_p{0, 0, 0};
     int c_it = 0;
 
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
@@ -169,7 +195,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // Q tiles of this wave (from the LDS stage, or straight from memory) into
     // MFMA B-operand registers
     auto read_q = [&]() {
-        const int64_t off = QSTAGE ? 0 : prob_offset(c_it);
+        const Prob qprob = QSTAGE ? Prob{0, 0, 0} : problem(c_it);
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             const int row = (wave * QT + t) * 16 + li;
@@ -178,7 +204,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                 if (QSTAGE) {
                     qreg[t][s] = *reinterpret_cast<const bf16x8*>(&qstage[row * G::KSTR + (4 * s + lg) * 8]);
                 } else {
-                    const int64_t a = off + (int64_t)tab[min(row, L - 1)] * row_stride + (4 * s + lg) * 8;
+                    const int64_t a = src_off(qprob, tab[min(row, L - 1)]) + (4 * s + lg) * 8;
                     qreg[t][s] = *reinterpret_cast<const bf16x8*>(qp + a);
                 }
             }
@@ -186,7 +212,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     };
 
     auto start_problem = [&]() {
-        cur_off = prob_offset(c_it);
+        cur_p = problem(c_it);
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             mrun[t] = -INFINITY;
@@ -289,8 +315,22 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             // hardware reciprocal (1 ulp) is exact enough for a bf16 output
             const float inv = __builtin_amdgcn_rcpf(osum[t][0]);
             const int row = (wave * QT + t) * 16 + li;
-            if (row < L) {
-                uint16_t* dst = op + cur_off + (int64_t)tab[row] * row_stride + 8 * lg;
+            // padded grids: real rows to out, padded rows of the local pass to
+            // the side buffer, padded rows of the global pass nowhere (cropped)
+            bool keep = row < L;
+            uint16_t* dst = op;
+            if (keep) {
+                const int tv = tab[row];
+                if (!PAD) {
+                    dst = op + cur_p.off + (int64_t)tv * row_stride + 8 * lg;
+                } else if (is_real(g, cur_p.base + tv)) {
+                    dst = op + src_off(cur_p, tv) + 8 * lg;
+                } else {
+                    keep = !GP;
+                    dst = yp + cur_p.yoff + (int64_t)pad_index(g, cur_p.base + tv) * row_stride + 8 * lg;
+                }
+            }
+            if (keep) {
 #pragma unroll
                 for (int p = 0; p < D / 32; ++p) {
                     bf16x8 o;
@@ -307,12 +347,12 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 
     // prologue: Q of the first problem straight into the stage, then PD steps in flight
     if (QSTAGE && nmine > 0) {
-        const int64_t off0 = prob_offset(0);
+        const Prob p0 = problem(0);
         for (int r = wave; r < NB * BR; r += blockDim.x >> 6) {
-            const int row = tab[min(r, L - 1)];
+            const int64_t a = src_off(p0, tab[min(r, L - 1)]);
             for (int c = lane; c < G::KC; c += 64)
                 *reinterpret_cast<u32x4*>(&qstage[r * G::KSTR + c * 8]) =
-                    *reinterpret_cast<const u32x4*>(qp + off0 + (int64_t)row * row_stride + c * 8);
+                    *reinterpret_cast<const u32x4*>(qp + a + c * 8);
         }
     }
 #pragma unroll
@@ -357,18 +397,18 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 }
 
 // The two passes as distinct kernels (so profiles tell them apart).
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_local_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
-    float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, false>(g, qp, kp, vp, op, scale_log2);
+    uint16_t* yp, float scale_log2) {
+    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD>(g, qp, kp, vp, op, yp, scale_log2);
 }
 
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_global_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
-    float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, true>(g, qp, kp, vp, op, scale_log2);
+    uint16_t* yp, float scale_log2) {
+    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD>(g, qp, kp, vp, op, yp, scale_log2);
 }
 
 int grid_for(const void* kern, int threads, int nprob) {
@@ -402,11 +442,11 @@ int grid_for(const void* kern, int threads, int nprob) {
 // d = 128, 4 at d = 64) so that every thread stages one chunk per tensor.  The
 // register budget follows the waves that share a SIMD (<= 12 waves: 168
 // VGPRs; 8 waves: 256); longer problems put 2, 3 or 4 tiles on each wave.
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE>
-hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o,
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD>
+hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o, void* y,
                       hipStream_t st) {
-    auto kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE>
-                        : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE>;
+    auto kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD>
+                        : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD>;
     const void* kern = reinterpret_cast<const void*>(kfn);
     const int threads = 64 * waves;
     if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.L > LMAX || (g.L + 15) / 16 > QT * waves)
@@ -415,26 +455,32 @@ hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k
     const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf((float)D);
     hipLaunchKernelGGL(kfn, dim3(grid), dim3(threads), 0, st, g, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
-                       scale_log2);
+                       static_cast<uint16_t*>(y), scale_log2);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const PassGeom& g, const void* q, const void* k, const void* v, void* o, hipStream_t st) {
+template <int D, bool PAD>
+hipError_t launch_d(const PassGeom& g, const void* q, const void* k, const void* v, void* o, void* y,
+                    hipStream_t st) {
     constexpr int minw = Geo<D>::NCH / 64;
     const int tiles = (g.L + 15) / 16;
-    if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true>(g, tiles > minw ? tiles : minw, q, k, v, o, st);
-    if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true>(g, 8, q, k, v, o, st);
-    if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true>(g, 8, q, k, v, o, st);
-    return launch_one<D, 4, 8, 2, 2, 512, false>(g, 8, q, k, v, o, st);
+    if (tiles <= 12)
+        return launch_one<D, 1, 12, 4, 3, 192, true, PAD>(g, tiles > minw ? tiles : minw, q, k, v, o, y, st);
+    if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD>(g, 8, q, k, v, o, y, st);
+    if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD>(g, 8, q, k, v, o, y, st);
+    return launch_one<D, 4, 8, 2, 2, 512, false, PAD>(g, 8, q, k, v, o, y, st);
 }
 
 }  // namespace
 
 hipError_t launch_pass_bf16(const PassGeom& g, int d, const void* q, const void* k, const void* vals, void* out,
-                            hipStream_t stream) {
-    if (d == 128) return launch_d<128>(g, q, k, vals, out, stream);
-    return launch_d<64>(g, q, k, vals, out, stream);
+                            void* ypad, hipStream_t stream) {
+    if (g.pad) {
+        if (d == 128) return launch_d<128, true>(g, q, k, vals, out, ypad, stream);
+        return launch_d<64, true>(g, q, k, vals, out, ypad, stream);
+    }
+    if (d == 128) return launch_d<128, false>(g, q, k, vals, out, nullptr, stream);
+    return launch_d<64, false>(g, q, k, vals, out, nullptr, stream);
 }
 
 }  // namespace squad

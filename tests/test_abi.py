@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(bd.ALL_SYMBOLS) == set(names)
     for n in names:
         assert getattr(lib, n) is not None
-    assert lib.squad_attn_abi_version() == 1
+    assert lib.squad_attn_abi_version() == 2
 
 
 def test_exports_via_nm():
@@ -161,7 +161,7 @@ def test_flops_and_bytes_helpers():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert isinstance(bd.status_str(s), str) and bd.status_str(s)
     assert bd.status_str(123) == "unknown status"
     assert bd.lib().squad_attn_last_hip_error() == 0
@@ -172,3 +172,98 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         bd.lib()
+
+
+# ---------------------------------------------------------------------------
+# Padded grids (window need not tile the grid)
+# ---------------------------------------------------------------------------
+
+# 5B grid with a 21x2x3 window: Ws = 40 padded to 42 (one mirrored column pair)
+PGEO = dict(B=1, heads=24, T=21, Hs=22, Ws=40, wt=21, wh=2, ww=3, d=128)
+PAD_BYTES = 1 * 21 * 22 * 2 * 24 * 128 * 2    # 21 frames x 22 rows x 2 padded columns
+WS = A + 16 * BYTES
+
+
+def pcall(fn="check", q=Q, k=K, v=V, out=O, ws=WS, ws_bytes=PAD_BYTES, dtype=bd.SQUAD_BF16, **over):
+    g = dict(PGEO)
+    g.update(over)
+    args = (q, k, v, out, ws, ws_bytes, g["B"], g["heads"], g["T"], g["Hs"], g["Ws"], g["wt"], g["wh"], g["ww"],
+            g["d"], dtype)
+    if fn == "check":
+        return bd.squad_attn_check_padded(*args)
+    return bd.lib().squad_attn_fwd_padded(*args, None)
+
+
+def test_padded_workspace_size():
+    assert bd.squad_attn_padded_workspace_bytes(*PGEO.values(), bd.SQUAD_BF16) == PAD_BYTES
+    assert bd.squad_attn_padded_workspace_bytes(*PGEO.values(), bd.SQUAD_F32) == 2 * PAD_BYTES
+    assert bd.squad_attn_padded_workspace_bytes(*GEO.values(), bd.SQUAD_BF16) == 0      # tiles: nothing padded
+    assert bd.squad_attn_padded_workspace_bytes(*GEO.values(), 5) == -1
+    g = dict(PGEO, wt=4)
+    assert bd.squad_attn_padded_workspace_bytes(*g.values(), bd.SQUAD_BF16) == -1      # T % wt != 0
+    # both margins: 2x5x7 grid, 2x3x2 window -> 2x6x8 padded, 48 - 35 = 13 padded positions per frame pair
+    assert bd.squad_attn_padded_workspace_bytes(1, 2, 2, 5, 7, 2, 3, 2, 64, bd.SQUAD_F32) == 2 * 13 * 2 * 64 * 4
+
+
+@pytest.mark.parametrize("fn", ["check", "fwd"])
+def test_padded_rejections(fn):
+    # every case is rejected on the host, so the compute entry point is safe to
+    # call with fake pointers; the check function must agree with it
+    S, U, N, W, AL, AS = (bd.SQUAD_ERR_SHAPE, bd.SQUAD_ERR_UNSUPPORTED, bd.SQUAD_ERR_NULL, bd.SQUAD_ERR_WORKSPACE,
+                          bd.SQUAD_ERR_ALIGN, bd.SQUAD_ERR_ALIAS)
+    assert pcall(fn, wt=4) == S                      # time axis never padded
+    assert pcall(fn, wh=23) == S                     # window taller than the grid: mirror would overrun
+    assert pcall(fn, ww=41) == S
+    assert pcall(fn, B=-1) == S
+    assert pcall(fn, T=8, Hs=8, Ws=8, wt=8, wh=8, ww=9) == S    # ww > Ws
+    assert pcall(fn, d=96) == U
+    assert pcall(fn, dtype=3) == U
+    assert pcall(fn, T=8, Hs=15, Ws=15, wt=8, wh=8, ww=9) == U  # m = 576 > 512
+    assert pcall(fn, T=1, Hs=1000, Ws=1100, wt=1, wh=100, ww=99, d=64) == U   # Wp = 1188 > 1023
+    assert pcall(fn, q=0) == N
+    assert pcall(fn, ws=0) == W
+    assert pcall(fn, ws_bytes=PAD_BYTES - 16) == W
+    assert pcall(fn, q=0, ws=0) == N                  # null before workspace
+    assert pcall(fn, ws=WS + 8) == AL
+    assert pcall(fn, out=O + 8) == AL
+    assert pcall(fn, ws=0, out=O + 8) == W            # workspace before align
+    assert pcall(fn, out=V) == AS                     # padded: no in-place over v
+    assert pcall(fn, out=K + 32) == AS
+    assert pcall(fn, ws=O + 32) == AS                 # workspace overlapping out
+    assert pcall(fn, ws=Q - PAD_BYTES + 16) == AS     # workspace tail over q
+
+
+def test_padded_check_accepts_what_would_launch():
+    assert pcall() == bd.SQUAD_OK
+    assert pcall(ws=Q - PAD_BYTES) == bd.SQUAD_OK                     # adjacent to q
+    assert pcall(T=8, Hs=15, Ws=15, wt=8, wh=8, ww=8) == bd.SQUAD_OK  # m = 512 on a 16x16 padded grid
+    # a window that tiles: workspace unused (NULL is fine) and out == v allowed
+    assert pcall(ww=4, ws=0, ws_bytes=0) == bd.SQUAD_OK
+    assert pcall(ww=4, ws=0, ws_bytes=0, out=V) == bd.SQUAD_OK
+    assert pcall(B=0, q=0, ws=0) == bd.SQUAD_OK
+    assert pcall("fwd", B=0, q=0, k=0, v=0, out=0, ws=0) == bd.SQUAD_OK   # empty: nothing enqueued
+
+
+def test_padded_flops_and_bytes_helpers():
+    for geo in [(1, 24, 21, 22, 40, 21, 2, 3, 128), (2, 3, 2, 5, 7, 2, 3, 2, 64), (1, 24, 21, 22, 40, 21, 2, 4, 128)]:
+        assert bd.squad_attn_flops_padded(*geo) == so.squad_flops_padded(*geo)
+        B, heads, T, Hs, Ws, wt, wh, ww, d = geo
+        _, Hp, Wp = so.padded_grid(T, Hs, Ws, wt, wh, ww)
+        n, n_p = T * Hs * Ws, T * Hp * Wp
+        assert bd.squad_attn_bytes_padded(*geo, bd.SQUAD_BF16) == (7 * n_p + n) * B * heads * d * 2
+    assert bd.squad_attn_flops_padded(1, 24, 21, 22, 40, 21, 2, 4, 128) == bd.squad_attn_flops(
+        1, 24, 21, 22, 40, 21, 2, 4, 128)
+    assert bd.squad_attn_flops_padded(1, 1, 21, 22, 40, 4, 2, 3, 128) == -1
+
+
+def test_window_solver_matches_oracle_rule():
+    for T in (1, 2, 21):
+        for Hs in range(1, 64, 5):
+            for Ws in range(1, 120, 9):
+                assert bd.squad_window_solve((T, Hs, Ws)) == so.solve_window(T, Hs, Ws), (T, Hs, Ws)
+    assert bd.squad_window_solve((21, 22, 40)) == (21, 2, 4)
+    assert bd.squad_window_solve((21, 30, 52)) == (21, 2, 4)
+    with pytest.raises(bd.SquadError):
+        bd.squad_window_solve((0, 4, 4))
+    with pytest.raises(bd.SquadError):
+        bd.squad_window_solve((1 << 11, 1 << 10, 1 << 10))
