@@ -4,7 +4,7 @@
  *
  * The operator (SQuad: Sub-Quadratic Attention Distillation for Efficient
  * Video Generation) replaces one full softmax self-attention over the n latent
- * tokens of a video DiT block by two ordinary softmax attentions composed
+ * tokens of a video DiT block by two plain softmax attentions composed
  * (agihunt.info summary, method paragraph; paperpeel full text, sec. 3.2):
  *
  *   local pass   Y[c,j] = sum_{j'} softmax_{j'}(<Q[c,j], K[c,j']> / sqrt(d)) V[c,j']
@@ -108,8 +108,8 @@ squad_status_t squad_attn_fwd_reversed(const void* q, const void* k, const void*
                                        int dtype, hipStream_t stream);
 
 /* Grids a window does not tile (paperpeel full text, appendix paragraph
- * "Conformance to the theoretical curves is quantitative": a window that does
- * not divide the latent grid is made to fit by a little reflect padding).
+ * "Conformance to the theoretical curves is quantitative": such windows are
+ * handled by extending the grid with mirror images).
  *
  * out = the real tokens of SQuad on the padded grid: the (T, Hs, Ws) grid is
  * extended at the bottom and right to (T, Hp, Wp), Hp = ceil(Hs/wh)*wh and

@@ -7,9 +7,9 @@ with the HIP path (it does not import the package; inputs arrive as arrays).
 What is computed (SQuad: Sub-Quadratic Attention Distillation for Efficient
 Video Generation):
 
-* The operator composes two ordinary softmax attentions run one after the other,
-  with only re-indexing in between, where the axis not attended over is folded
-  into the head count (agihunt.info summary, method paragraph; paperpeel full
+* The operator composes two plain softmax attentions run one after the other,
+  with only re-indexing in between, every position along the axis a pass does
+  not attend over acting as one more head (agihunt.info summary, method paragraph; paperpeel full
   text, sec. 3.2 and appendix E "Cost of the two passes").
 * Local pass: tokens mix within fixed windows of about sqrt(n) tokens, cut from
   the latent grid and spanning the whole temporal extent (agihunt.info summary;
@@ -69,7 +69,7 @@ def window_slot_table(T, Hs, Ws, wt, wh, ww):
 
 
 # ---------------------------------------------------------------------------
-# One ordinary softmax attention
+# One plain softmax attention
 # ---------------------------------------------------------------------------
 
 def softmax_attention(q, k, v):
@@ -96,7 +96,7 @@ def local_pass_head(q, k, v, table):
     """Attn_L: every window attends within itself.  q, k, v: [n, d] -> [n, d]."""
     out = np.empty(np.shape(v), dtype=np.float64)
     # gather [N_w, m, d]: the attended axis (slots) becomes the sequence, the
-    # window axis is folded into the batch/head count
+    # each window is an independent attention (a batch entry)
     out[table] = softmax_attention(q[table], k[table], v[table])
     return out
 
@@ -234,8 +234,8 @@ def full_attention_flops(B, heads, n, d):
 # curves is quantitative": the window is chosen afresh for every latent grid so
 # that its volume m follows sqrt(n); it always spans the whole temporal extent
 # (wt = T) and its spatial extents keep the grid's aspect ratio; m must be a
-# whole number of tokens, and a window that does not divide the grid is made to
-# fit by a little reflect padding.  The pages print no formula beyond this.
+# whole number of tokens, and where the window does not divide the grid the grid
+# is extended with mirror images.  The pages print no formula beyond this.
 # Reading taken: the continuous optimum has wt = T, wh * ww = sqrt(n) / T and
 # wh : ww = Hs : Ws; each spatial extent is rounded down or up (kept within
 # 1..extent), and of those (at most four) windows the one with the least
