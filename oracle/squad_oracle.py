@@ -95,8 +95,8 @@ def softmax_attention(q, k, v):
 def local_pass_head(q, k, v, table):
     """Attn_L: every window attends within itself.  q, k, v: [n, d] -> [n, d]."""
     out = np.empty(np.shape(v), dtype=np.float64)
-    # gather [N_w, m, d]: the attended axis (slots) becomes the sequence, the
-    # each window is an independent attention (a batch entry)
+    # gather [N_w, m, d]: the slots of a window form the sequence and each
+    # window is an independent attention (a batch entry)
     out[table] = softmax_attention(q[table], k[table], v[table])
     return out
 
@@ -334,3 +334,78 @@ def squad_flops_padded(B, heads, T, Hs, Ws, wt, wh, ww, d):
     """FLOPs of the operator on the padded grid (the work actually done)."""
     _, Hp, Wp = padded_grid(T, Hs, Ws, wt, wh, ww)
     return squad_flops(B, heads, T, Hp, Wp, wt, wh, ww, d)
+
+
+
+# ---------------------------------------------------------------------------
+# Gradients (the backward pass)
+# ---------------------------------------------------------------------------
+#
+# The pages train through the operator (flow-matching fine-tuning and DMD2
+# distillation, SQuad paper sec. 3.3 and sec. 4), so it must be differentiated;
+# they print no backward.  What follows is the chain rule applied to the two
+# softmax attentions as defined above, nothing else: for one attention
+# O = P V with P = softmax(S) and S = Q K^T / sqrt(d), and an upstream
+# gradient dO,
+#     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+#     dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d)
+# (rowsum(P * dP) = rowsum(dO * O) is the softmax Jacobian's correction).
+# SQuad: O = Attn_G(Q, K, Y) with Y = Attn_L(Q, K, V); the global pass's value
+# gradient is the local pass's upstream gradient, and Q and K collect
+# contributions from both passes.
+
+def softmax_attention_backward(q, k, v, do):
+    """(dq, dk, dv) of softmax(q k^T / sqrt(d)) v over the last two axes, float64."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    d = q.shape[-1]
+    s = q @ np.swapaxes(k, -1, -2) / math.sqrt(d)
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    dv = np.swapaxes(p, -1, -2) @ do
+    dp = do @ np.swapaxes(v, -1, -2)
+    ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+    dq = ds @ k / math.sqrt(d)
+    dk = np.swapaxes(ds, -1, -2) @ q / math.sqrt(d)
+    return dq, dk, dv
+
+
+def _pass_backward(q, k, vals, dout, rows):
+    """Backward of one pass whose problems are the rows of the index table
+    `rows` ([problems, L] token indices): gradients in token order."""
+    dq, dk, dvals = softmax_attention_backward(q[rows], k[rows], vals[rows], dout[rows])
+    gq, gk, gv = (np.empty(np.shape(q), dtype=np.float64) for _ in range(3))
+    gq[rows], gk[rows], gv[rows] = dq, dk, dvals
+    return gq, gk, gv
+
+
+def squad_backward_head(q, k, v, do, table):
+    """(dQ, dK, dV) of O = Attn_G(Q, K, Attn_L(Q, K, V)) for one head, given
+    dO; [n, d] each.  The local output Y is recomputed."""
+    y = local_pass_head(q, k, v, table)
+    dq_g, dk_g, dy = _pass_backward(q, k, y, do, np.ascontiguousarray(table.T))
+    dq_l, dk_l, dv = _pass_backward(q, k, v, dy, table)
+    return dq_l + dq_g, dk_l + dk_g, dv
+
+
+def squad_backward(q, k, v, do, geom):
+    """Whole-tensor gradients for [B, n, heads, d] inputs; geom as squad_attention."""
+    B, heads, T, Hs, Ws, wt, wh, ww, d = geom
+    table = window_slot_table(T, Hs, Ws, wt, wh, ww)
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    out = [np.empty(q.shape, dtype=np.float64) for _ in range(3)]
+    for b in range(B):
+        for h in range(heads):
+            g = squad_backward_head(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], table)
+            for o, gi in zip(out, g):
+                o[b, :, h] = gi
+    return tuple(out)
+
+
+def squad_backward_flops(B, heads, T, Hs, Ws, wt, wh, ww, d):
+    """FLOPs of the gradients counted like the forward's (2 per multiply-add
+    of each matmul): per attention of length L the scores S and the four
+    products dP, dV, dQ, dK, five L x L x d products against the forward's
+    two, so 2.5 times squad_flops (recomputing the local output, which the
+    forward does not keep, is not counted here)."""
+    return 5 * squad_flops(B, heads, T, Hs, Ws, wt, wh, ww, d) // 2
