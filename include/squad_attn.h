@@ -182,6 +182,64 @@ double squad_attn_bytes_padded(int B, int heads, int T, int Hs, int Ws,
  * function. */
 squad_status_t squad_window_solve(int T, int Hs, int Ws, int* wt, int* wh, int* ww);
 
+/* Gradients of squad_attn_fwd (the chain rule of its two softmax attentions;
+ * the pages train through the operator, SQuad paper sec. 3.3 and sec. 4, but
+ * print no backward):
+ *   global pass O = Attn_G(q, k, Y):  dY, and dq, dk contributions;
+ *   local pass  Y = Attn_L(q, k, v):  dv, and dq, dk contributions with dY as
+ *                                     the upstream gradient;
+ * where for one attention with P = softmax(q k^T / sqrt(d)), D = rowsum(dO*O),
+ * dS = P * (dO v^T - D): dq = dS k / sqrt(d), dk = dS^T q / sqrt(d),
+ * dv = P^T dO.
+ *
+ * q, k, v: the forward's inputs; out: its output O; dout: dL/dO; dq, dk, dv:
+ * receive dL/dq, dL/dk, dL/dv.  All [B, n, heads, d] of one dtype, as for
+ * squad_attn_fwd (windows must tile the grid).  workspace: device buffer of at
+ * least squad_attn_bwd_workspace_bytes(...) bytes, 16-byte aligned: the
+ * recomputed local output Y and dY in the dtype and float32 partial dq, dk
+ * (contents on entry ignored; one workspace must not serve calls that may run
+ * at the same time).  Three kernels are enqueued on `stream`: the local pass
+ * (recomputing Y), the global pass's backward, the local pass's backward.
+ * P and dS enter the bf16 MFMAs rounded to bf16; sums are float32.
+ *
+ * Errors as squad_attn_fwd for the shape, dtype and sizes; SQUAD_ERR_NULL for
+ * any NULL tensor; SQUAD_ERR_WORKSPACE for a NULL or too small workspace;
+ * SQUAD_ERR_ALIGN for any pointer not 16-byte aligned; SQUAD_ERR_ALIAS if a
+ * gradient overlaps an input, another gradient or the workspace, or the
+ * workspace overlaps an input (inputs may overlap one another). */
+squad_status_t squad_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                              int B, int heads, int T, int Hs, int Ws,
+                              int wt, int wh, int ww, int d,
+                              int dtype, hipStream_t stream);
+
+/* Validation only for squad_attn_bwd (pure host function). */
+squad_status_t squad_attn_check_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                    const void* dq, const void* dk, const void* dv,
+                                    const void* workspace, size_t workspace_bytes,
+                                    int B, int heads, int T, int Hs, int Ws,
+                                    int wt, int wh, int ww, int d, int dtype);
+
+/* Bytes of workspace squad_attn_bwd needs (0 for an empty problem, -1 on a
+ * shape or dtype it rejects).  Pure host function. */
+long long squad_attn_bwd_workspace_bytes(int B, int heads, int T, int Hs, int Ws,
+                                         int wt, int wh, int ww, int d, int dtype);
+
+/* FLOPs of the gradients counted like squad_attn_flops: per attention the
+ * scores and the products dP, dV, dQ, dK, i.e. 2.5 * squad_attn_flops
+ * (recomputing Y is not counted).  -1 on a rejected shape.  Pure host
+ * function. */
+double squad_attn_bwd_flops(int B, int heads, int T, int Hs, int Ws,
+                            int wt, int wh, int ww, int d);
+
+/* HBM bytes of one squad_attn_bwd call as its three kernels move them:
+ * E*sizeof(dtype)*18 + E*16 with E = B*n*heads*d (recompute of Y: 3 reads, 1
+ * write; global backward: q, k, Y, O, dO read, dY written, float32 dq, dk
+ * written; local backward: q, k, v, Y, dY read, float32 partials read, dq, dk,
+ * dv written).  -1 on a rejected shape or dtype.  Pure host function. */
+double squad_attn_bwd_bytes(int B, int heads, int T, int Hs, int Ws,
+                            int wt, int wh, int ww, int d, int dtype);
+
 /* Validation only: the status any compute entry point would return for these
  * arguments before launching (SQUAD_OK when it would launch).  Pure host
  * function: makes no HIP call and never dereferences the pointers. */
@@ -213,8 +271,8 @@ const char* squad_status_str(int status);
  * (0 if none). */
 int squad_attn_last_hip_error(void);
 
-/* Version of this ABI (bumped on any incompatible change; 2 adds the padded
- * entry points and SQUAD_ERR_WORKSPACE). */
+/* Version of this ABI (bumped on any change; 2 adds the padded entry points,
+ * the backward and SQUAD_ERR_WORKSPACE). */
 int squad_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -11,6 +11,10 @@ from .binding import (  # noqa: F401
     SQUAD_BF16,
     SQUAD_F32,
     SquadError,
+    squad_attn_bwd,
+    squad_attn_bwd_bytes,
+    squad_attn_bwd_flops,
+    squad_attn_bwd_workspace_bytes,
     squad_attn_bytes,
     squad_attn_flops,
     squad_attn_bytes_padded,

@@ -33,6 +33,8 @@ COMPUTE_ENTRY_POINTS = ("squad_attn_fwd", "squad_attn_local", "squad_attn_global
 ALL_SYMBOLS = COMPUTE_ENTRY_POINTS + (
     "squad_attn_fwd_padded", "squad_attn_check_padded", "squad_attn_padded_workspace_bytes",
     "squad_attn_flops_padded", "squad_attn_bytes_padded", "squad_window_solve",
+    "squad_attn_bwd", "squad_attn_check_bwd", "squad_attn_bwd_workspace_bytes", "squad_attn_bwd_flops",
+    "squad_attn_bwd_bytes",
     "squad_attn_check", "squad_attn_max_len", "squad_attn_flops", "squad_attn_bytes", "squad_status_str",
     "squad_attn_last_hip_error", "squad_attn_abi_version",
 )
@@ -77,6 +79,16 @@ def lib() -> ctypes.CDLL:
     L.squad_attn_bytes_padded.restype = d
     L.squad_window_solve.argtypes = [i, i, i, ip, ip, ip]
     L.squad_window_solve.restype = i
+    L.squad_attn_bwd.argtypes = [p] * 9 + [sz] + [i] * 10 + [p]
+    L.squad_attn_bwd.restype = i
+    L.squad_attn_check_bwd.argtypes = [p] * 9 + [sz] + [i] * 10
+    L.squad_attn_check_bwd.restype = i
+    L.squad_attn_bwd_workspace_bytes.argtypes = [i] * 10
+    L.squad_attn_bwd_workspace_bytes.restype = ctypes.c_longlong
+    L.squad_attn_bwd_flops.argtypes = [i] * 9
+    L.squad_attn_bwd_flops.restype = d
+    L.squad_attn_bwd_bytes.argtypes = [i] * 10
+    L.squad_attn_bwd_bytes.restype = d
     L.squad_attn_max_len.argtypes = [i, i]
     L.squad_attn_max_len.restype = i
     L.squad_attn_flops.argtypes = [i] * 9
@@ -142,6 +154,25 @@ def squad_attn_flops_padded(B, heads, T, Hs, Ws, wt, wh, ww, d) -> float:
 
 def squad_attn_bytes_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> float:
     return lib().squad_attn_bytes_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_attn_bwd_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> int:
+    return lib().squad_attn_bwd_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_attn_bwd_flops(B, heads, T, Hs, Ws, wt, wh, ww, d) -> float:
+    return lib().squad_attn_bwd_flops(B, heads, T, Hs, Ws, wt, wh, ww, d)
+
+
+def squad_attn_bwd_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> float:
+    return lib().squad_attn_bwd_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_attn_check_bwd(q, k, v, out, dout, dq, dk, dv, ws, ws_bytes, B, heads, T, Hs, Ws, wt, wh, ww, d,
+                         dtype) -> int:
+    """Host-only validation status of squad_attn_bwd for raw pointers."""
+    return lib().squad_attn_check_bwd(q, k, v, out, dout, dq, dk, dv, ws, ws_bytes, B, heads, T, Hs, Ws, wt, wh, ww,
+                                      d, dtype)
 
 
 def squad_attn_check_padded(q, k, v, out, ws, ws_bytes, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> int:
@@ -243,3 +274,39 @@ def squad_attn_fwd_padded(q, k, v, grid, window, out=None, workspace=None, strea
     if st != SQUAD_OK:
         raise SquadError(st, "squad_attn_fwd_padded")
     return out
+
+
+def squad_attn_bwd(q, k, v, out, dout, grid, window, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """(dq, dk, dv) of squad_attn_fwd at (q, k, v), given its output `out` and
+    the upstream gradient `dout`.  `workspace`: a device tensor of at least
+    squad_attn_bwd_workspace_bytes bytes (allocated through torch if None)."""
+    import torch
+    _check_tensors(q, k, v, None, grid)
+    for t in (out, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("out and dout must be contiguous tensors like q")
+    dq, dk, dv = (torch.empty_like(q) if t is None else t for t in (dq, dk, dv))
+    for t in (dq, dk, dv):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous tensors like q")
+    B, n, heads, d = q.shape
+    T, Hs, Ws = grid
+    wt, wh, ww = window
+    dt = _dtype_code(q)
+    need = squad_attn_bwd_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dt)
+    if need < 0:
+        raise SquadError(SQUAD_ERR_SHAPE, "squad_attn_bwd")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().squad_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                  B, heads, T, Hs, Ws, wt, wh, ww, d, dt, stream)
+    if st != SQUAD_OK:
+        raise SquadError(st, "squad_attn_bwd")
+    return dq, dk, dv

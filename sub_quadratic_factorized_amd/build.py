@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libsquad_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["squad_abi.hip", "squad_pass_bf16.hip", "squad_pass_f32.hip"]
+SOURCES = ["squad_abi.hip", "squad_pass_bf16.hip", "squad_pass_f32.hip", "squad_bwd_bf16.hip", "squad_bwd_f32.hip"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

@@ -222,6 +222,84 @@ hipError_t run_two_passes(const Problem& pr, bool local_first, const void* q, co
     return e;
 }
 
+// Workspace of the backward: Y (the recomputed local output) and dY in the
+// dtype, then the global pass's float32 contributions to dQ and dK; each
+// region starts on a 256-byte boundary.
+struct BwdLayout {
+    size_t y, dy, gq, gk, total;
+};
+
+BwdLayout bwd_layout(const Problem& pr) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t e = (size_t)pr.elems;
+    BwdLayout l;
+    l.y = 0;
+    l.dy = up(e * esize(pr.dtype));
+    l.gq = l.dy + up(e * esize(pr.dtype));
+    l.gk = l.gq + up(e * 4);
+    l.total = l.gk + up(e * 4);
+    return l;
+}
+
+// Arguments of squad_attn_bwd: the forward's checks on (q, k, v, out), then
+// dout and the three gradients, then the workspace; gradients must not overlap
+// any input, one another or the workspace.
+squad_status_t validate_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                            const void* dq, const void* dk, const void* dv, const void* ws, size_t ws_size, int B,
+                            int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype, Problem* pr,
+                            bool* empty) {
+    squad_status_t s = check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, pr, empty);
+    if (s != SQUAD_OK) return s;
+    if (*empty) return SQUAD_OK;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return SQUAD_ERR_UNSUPPORTED;
+    const int maxlen = squad_attn_max_len(d, dtype);
+    if (maxlen == 0) return SQUAD_ERR_UNSUPPORTED;
+    if (pr->m > maxlen || pr->nw > maxlen) return SQUAD_ERR_UNSUPPORTED;
+    pr->dtype = dtype;
+    if (!q || !k || !v || !out || !dout || !dq || !dk || !dv) return SQUAD_ERR_NULL;
+    const BwdLayout lay = bwd_layout(*pr);
+    if (!ws || ws_size < lay.total) return SQUAD_ERR_WORKSPACE;
+    const uintptr_t bits = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout |
+                           (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)ws;
+    if (bits & 15u) return SQUAD_ERR_ALIGN;
+    pr->bytes = (size_t)pr->elems * (size_t)esize(dtype);
+    const void* grads[3] = {dq, dk, dv};
+    const void* ins[5] = {q, k, v, out, dout};
+    const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + lay.total;
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(grads[i], ins[j], pr->bytes)) return SQUAD_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(grads[i], grads[j], pr->bytes)) return SQUAD_ERR_ALIAS;
+    }
+    for (const void* t : {q, k, v, out, dout, dq, dk, dv}) {
+        const uintptr_t a = (uintptr_t)t;
+        if (a < w1 && w0 < a + pr->bytes) return SQUAD_ERR_ALIAS;
+    }
+    return SQUAD_OK;
+}
+
+hipError_t run_backward(const Problem& pr, const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
+    const BwdLayout lay = bwd_layout(pr);
+    char* w = static_cast<char*>(ws);
+    void *y = w + lay.y, *dy = w + lay.dy;
+    float *gq = reinterpret_cast<float*>(w + lay.gq), *gk = reinterpret_cast<float*>(w + lay.gk);
+    // the forward keeps only O: recompute the local output Y
+    hipError_t e = run_pass(pr, false, q, k, v, y, nullptr, st);
+    if (e != hipSuccess) return e;
+    const bool bf16 = pr.dtype == SQUAD_BF16;
+    // global pass (values Y, output O): dQ, dK contributions in float32, dY
+    const PassGeom gg = make_geom(pr, true);
+    BwdArgs ag{q, k, y, out, dout, nullptr, nullptr, gq, gk, dy, true};
+    e = bf16 ? launch_bwd_pass_bf16(gg, pr.d, ag, st) : launch_bwd_pass_f32(gg, pr.d, ag, st);
+    if (e != hipSuccess) return e;
+    // local pass (values V, output Y, upstream dY): adds the global pass's share
+    const PassGeom gl = make_geom(pr, false);
+    BwdArgs al{q, k, v, y, dy, gq, gk, dq, dk, dv, !bf16};
+    return bf16 ? launch_bwd_pass_bf16(gl, pr.d, al, st) : launch_bwd_pass_f32(gl, pr.d, al, st);
+}
+
 squad_status_t hip_status(hipError_t e) {
     if (e == hipSuccess) return SQUAD_OK;
     g_last_hip_error = (int)e;
@@ -399,6 +477,56 @@ squad_status_t squad_window_solve(int T, int Hs, int Ws, int* wt, int* wh, int* 
     squad::solve_window(T, Hs, Ws, wh, ww);
     *wt = T;
     return SQUAD_OK;
+}
+
+squad_status_t squad_attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int heads,
+                              int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype, hipStream_t stream) {
+    squad::Problem pr;
+    bool empty = false;
+    const squad_status_t s = squad::validate_bwd(q, k, v, out, dout, dq, dk, dv, workspace, workspace_bytes, B,
+                                                 heads, T, Hs, Ws, wt, wh, ww, d, dtype, &pr, &empty);
+    if (s != SQUAD_OK || empty) return s;
+    return squad::hip_status(squad::run_backward(pr, q, k, v, out, dout, dq, dk, dv, workspace, stream));
+}
+
+squad_status_t squad_attn_check_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                    const void* dq, const void* dk, const void* dv, const void* workspace,
+                                    size_t workspace_bytes, int B, int heads, int T, int Hs, int Ws, int wt, int wh,
+                                    int ww, int d, int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    return squad::validate_bwd(q, k, v, out, dout, dq, dk, dv, workspace, workspace_bytes, B, heads, T, Hs, Ws, wt,
+                               wh, ww, d, dtype, &pr, &empty);
+}
+
+long long squad_attn_bwd_workspace_bytes(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d,
+                                         int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return -1;
+    if (squad::check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1;
+    if (empty) return 0;
+    pr.dtype = dtype;
+    return (long long)squad::bwd_layout(pr).total;
+}
+
+double squad_attn_bwd_flops(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d) {
+    const double f = squad_attn_flops(B, heads, T, Hs, Ws, wt, wh, ww, d);
+    return f < 0 ? f : 2.5 * f;
+}
+
+double squad_attn_bwd_bytes(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return -1.0;
+    if (squad::check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1.0;
+    if (empty) return 0.0;
+    const double e = (double)pr.elems, es = squad::esize(dtype);
+    // recompute Y: 3 reads + 1 write; global pass: q, k, Y, O, dO read, dY
+    // written, float32 dQ and dK written; local pass: q, k, v, Y, dY and the
+    // float32 partials read, dq, dk, dv written
+    return e * es * (4.0 + 6.0 + 8.0) + e * 4.0 * 4.0;
 }
 
 squad_status_t squad_attn_check(const void* q, const void* k, const void* v, const void* out, int B, int heads,

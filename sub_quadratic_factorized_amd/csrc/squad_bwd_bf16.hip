@@ -1,0 +1,308 @@
+// bf16 MFMA backward of one SQuad-Attention pass on gfx950.
+//
+// A pass is a batch of independent softmax attentions O = P V with
+// P = softmax(S), S = Q K^T / sqrt(d), over the rows of a problem (PassGeom).
+// Given O and the upstream gradient dO (chain rule of softmax attention):
+//     D = rowsum(dO * O),  dP = dO V^T,  dS = P * (dP - D),
+//     dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
+//
+// One workgroup of 8 waves per problem; rows stream through LDS in blocks of
+// 32 (clamped past the end, masked).  Two kinds of MFMA product occur, both
+// on v_mfma_f32_16x16x32_bf16 with the operand layouts of the forward kernel:
+//   * over d (S, dP): both operands are token rows, read as 16-byte row
+//     chunks (the K/Q row layout in LDS, or registers loaded from memory);
+//   * over tokens (dQ^T = K^T dS^T, dV^T = dO^T P, dK^T = Q^T dS): the A
+//     operand is a block read transposed (the V layout and ds_read_b64_tr_b16
+//     fetch of the forward kernel), the B operand is a 16x16 result tile pair
+//     of the first kind packed to bf16 (its rows are the contracted tokens).
+// Query sweep (waves own 16-query tiles): a pass over K for the row maximum
+// and log-sum-exp, D from dO and O, then a pass over K and V accumulating
+// dQ^T.  Key sweep (waves own 16-key tiles): a pass over Q and dO
+// accumulating dV^T and dK^T from P and dS recomputed with the stored
+// log-sum-exp and D.  P and dS enter their MFMAs rounded to bf16; all sums
+// are float32.
+#include "squad_internal.h"
+#include "squad_layout.h"
+#include "squad_mfma.h"
+
+namespace squad {
+namespace {
+
+constexpr int BR = kBlockRows;
+constexpr int NW = 8;  // waves per workgroup
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[4]) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = static_cast<__bf16>(lo[i]);
+        r[4 + i] = static_cast<__bf16>(hi[i]);
+    }
+    return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
+    PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint16_t* __restrict__ op, const uint16_t* __restrict__ dop, const float* __restrict__ addq,
+    const float* __restrict__ addk, void* __restrict__ dqp, void* __restrict__ dkp, uint16_t* __restrict__ dvp,
+    int qk_f32, float c_log2, float scale) {
+    using G = BlockGeo<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t rowA[BR * G::KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t rowB[BR * G::KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t trA[BR * G::VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t trB[BR * G::VSTR];
+    __shared__ float lse[kMaxLen], dd[kMaxLen];
+    __shared__ int tab[kMaxLen];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int L = g.L;
+    const int NB = (L + BR - 1) / BR;
+    const int ntiles = (L + 15) / 16;
+    const int ngroups = (ntiles + NW - 1) / NW;
+    const int row_stride = g.heads * D;
+
+    const ProblemIndex pr = decode_problem(g, blockIdx.x);
+    const int base = g.global ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
+    const int64_t bh = (int64_t)pr.b * g.n * row_stride + (int64_t)pr.h * D;
+    for (int r = tid; r < L; r += blockDim.x) tab[r] = g.global ? win_origin(g, r) : slot_offset(g, r);
+    __syncthreads();
+    // element offset of row r of the problem (rows past the end clamped)
+    auto row = [&](int r) -> int64_t { return bh + (int64_t)(base + tab[min(r, L - 1)]) * row_stride; };
+
+    // rows blk*32 .. +31 of x into the row layout and / or the transposed-read layout
+    auto stage = [&](const uint16_t* x, int blk, uint16_t* rb, uint16_t* tb) {
+        for (int c = tid; c < G::NCH; c += 64 * NW) {
+            const int r = c / G::KC, col = (c % G::KC) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(x + row(blk * BR + r) + col);
+            if (rb) *reinterpret_cast<u32x4*>(&rb[r * G::KSTR + col]) = v;
+            if (tb)
+                *reinterpret_cast<u32x4*>(&tb[v_chunk_offset<D>(r, col / 8)]) =
+                    v_halves_swapped<D>(r) ? u32x4{v.z, v.w, v.x, v.y} : v;
+        }
+    };
+    // a 16-row tile of x as the row operand (lane: row li, d = 32s + 8lg ..)
+    auto load_tile = [&](const uint16_t* x, int tile, bf16x8 (&reg)[G::KS]) {
+        const int64_t a = row(tile * 16 + li);
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) reg[s] = *reinterpret_cast<const bf16x8*>(x + a + (4 * s + lg) * 8);
+    };
+    auto row_op = [&](const uint16_t* rb, int half, int s) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(&rb[(half * 16 + li) * G::KSTR + (4 * s + lg) * 8]);
+    };
+    const int vr = v_fetch_row(li, lg);
+    auto tr_op = [&](uint16_t* tb, int dt) -> bf16x8 {
+        const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&tb[off]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&tb[off + 16 * G::VSTR]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+    };
+    // a transposed accumulator (rows d as the forward output tiles, column =
+    // token li of `tile`) times `mul`, plus an optional float32 addend, stored
+    // to the token's row (8 consecutive d per lane and tile pair)
+    auto store_rows = [&](const f32x4 (&acc)[G::DT], float mul, int tile, const float* add, void* dst, bool f32) {
+        const int r = tile * 16 + li;
+        if (r >= L) return;
+        const int64_t a = row(r) + 8 * lg;
+#pragma unroll
+        for (int p = 0; p < D / 32; ++p) {
+            float o[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                o[i] = acc[2 * p][i] * mul;
+                o[4 + i] = acc[2 * p + 1][i] * mul;
+            }
+            if (add) {
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(add + a + 32 * p);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(add + a + 32 * p + 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    o[i] += x0[i];
+                    o[4 + i] += x1[i];
+                }
+            }
+            if (f32) {
+                float* d32 = static_cast<float*>(dst) + a + 32 * p;
+                *reinterpret_cast<f32x4*>(d32) = f32x4{o[0], o[1], o[2], o[3]};
+                *reinterpret_cast<f32x4*>(d32 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+            } else {
+                bf16x8 b;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) b[e] = static_cast<__bf16>(o[e]);
+                *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(dst) + a + 32 * p) = b;
+            }
+        }
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- query sweep: log-sum-exp, D, dQ ------------------------------------
+    for (int grp = 0; grp < ngroups; ++grp) {
+        const int qt = grp * NW + wave;
+        const bool active = qt < ntiles;
+        bf16x8 qreg[G::KS], doreg[G::KS];
+        float Dq = 0.0f;
+        if (active) {
+            load_tile(qp, qt, qreg);
+            load_tile(dop, qt, doreg);
+            const int64_t a = row(qt * 16 + li);
+            float part = 0.0f;
+#pragma unroll
+            for (int s = 0; s < G::KS; ++s) {
+                const bf16x8 o = *reinterpret_cast<const bf16x8*>(op + a + (4 * s + lg) * 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[s][e], (float)o[e], part);
+            }
+            Dq = row_sum4(part);
+        }
+        // scores S^T (keys x this wave's queries): row maximum and sum of exp2
+        float m = -INFINITY, l = 0.0f;
+        for (int kb = 0; kb < NB; ++kb) {
+            __syncthreads();
+            stage(kp, kb, rowA, nullptr);
+            __syncthreads();
+            if (active) {
+                f32x4 s0 = zero, s1 = zero;
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    s0 = mfma(row_op(rowA, 0, s), qreg[s], s0);
+                    s1 = mfma(row_op(rowA, 1, s), qreg[s], s1);
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (kb * BR + 4 * lg + i >= L) s0[i] = -INFINITY;
+                    if (kb * BR + 16 + 4 * lg + i >= L) s1[i] = -INFINITY;
+                    mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+                }
+                const float mnew = fmaxf(m, row_max4(mx) * c_log2);
+                float part = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    part += __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -mnew)) +
+                            __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -mnew));
+                l = l * __builtin_amdgcn_exp2f(m - mnew) + row_sum4(part);
+                m = mnew;
+            }
+        }
+        const float lse2 = m + __builtin_log2f(l);
+        if (active && lg == 0 && qt * 16 + li < L) {
+            lse[qt * 16 + li] = lse2;
+            dd[qt * 16 + li] = Dq;
+        }
+        // dQ^T += K^T dS^T over key blocks
+        f32x4 dqacc[G::DT];
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
+        for (int kb = 0; kb < NB; ++kb) {
+            __syncthreads();
+            stage(kp, kb, rowA, trA);
+            stage(vp, kb, rowB, nullptr);
+            __syncthreads();
+            if (active) {
+                f32x4 s0 = zero, s1 = zero, p0 = zero, p1 = zero;
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    s0 = mfma(row_op(rowA, 0, s), qreg[s], s0);
+                    s1 = mfma(row_op(rowA, 1, s), qreg[s], s1);
+                    p0 = mfma(row_op(rowB, 0, s), doreg[s], p0);  // dP^T
+                    p1 = mfma(row_op(rowB, 1, s), doreg[s], p1);
+                }
+                float ds0[4], ds1[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool v0 = kb * BR + 4 * lg + i < L, v1 = kb * BR + 16 + 4 * lg + i < L;
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -lse2));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -lse2));
+                    ds0[i] = v0 ? e0 * (p0[i] - Dq) : 0.0f;
+                    ds1[i] = v1 ? e1 * (p1[i] - Dq) : 0.0f;
+                }
+                const bf16x8 dsk = pack8(ds0, ds1);
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = mfma(tr_op(trA, dt), dsk, dqacc[dt]);
+            }
+        }
+        if (active) store_rows(dqacc, scale, qt, addq, dqp, qk_f32 != 0);
+    }
+    __syncthreads();  // every row's log-sum-exp and D are in LDS
+
+    // ---- key sweep: dV, dK ---------------------------------------------------
+    for (int grp = 0; grp < ngroups; ++grp) {
+        const int kt = grp * NW + wave;
+        const bool active = kt < ntiles;
+        bf16x8 kreg[G::KS], vreg[G::KS];
+        if (active) {
+            load_tile(kp, kt, kreg);
+            load_tile(vp, kt, vreg);
+        }
+        f32x4 dkacc[G::DT], dvacc[G::DT];
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt) dkacc[dt] = dvacc[dt] = zero;
+        for (int qb = 0; qb < NB; ++qb) {
+            __syncthreads();
+            stage(qp, qb, rowA, trA);
+            stage(dop, qb, rowB, trB);
+            __syncthreads();
+            if (active) {
+                f32x4 s0 = zero, s1 = zero, p0 = zero, p1 = zero;
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    s0 = mfma(row_op(rowA, 0, s), kreg[s], s0);  // S (queries x this wave's keys)
+                    s1 = mfma(row_op(rowA, 1, s), kreg[s], s1);
+                    p0 = mfma(row_op(rowB, 0, s), vreg[s], p0);  // dP
+                    p1 = mfma(row_op(rowB, 1, s), vreg[s], p1);
+                }
+                float pr0[4], pr1[4], ds0[4], ds1[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int q0 = qb * BR + 4 * lg + i, q1 = q0 + 16;
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -lse[q0]));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -lse[q1]));
+                    pr0[i] = q0 < L ? e0 : 0.0f;
+                    pr1[i] = q1 < L ? e1 : 0.0f;
+                    ds0[i] = q0 < L ? e0 * (p0[i] - dd[q0]) : 0.0f;
+                    ds1[i] = q1 < L ? e1 * (p1[i] - dd[q1]) : 0.0f;
+                }
+                const bf16x8 pp = pack8(pr0, pr1), dsp = pack8(ds0, ds1);
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt) {
+                    dvacc[dt] = mfma(tr_op(trB, dt), pp, dvacc[dt]);
+                    dkacc[dt] = mfma(tr_op(trA, dt), dsp, dkacc[dt]);
+                }
+            }
+        }
+        if (active) {
+            store_rows(dkacc, scale, kt, addk, dkp, qk_f32 != 0);
+            store_rows(dvacc, 1.0f, kt, nullptr, dvp, false);
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
+    const float scale = 1.0f / __builtin_sqrtf((float)D);
+    const float c_log2 = 1.4426950408889634f * scale;
+    hipLaunchKernelGGL(squad_bwd_pass_bf16<D>, dim3(g.nprob), dim3(64 * NW), 0, st, g,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.vals), static_cast<const uint16_t*>(a.out),
+                       static_cast<const uint16_t*>(a.dout), a.addq, a.addk, a.dq, a.dk,
+                       static_cast<uint16_t*>(a.dvals), a.qk_f32 ? 1 : 0, c_log2, scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream) {
+    if (d == 128) return launch_d<128>(g, a, stream);
+    return launch_d<64>(g, a, stream);
+}
+
+}  // namespace squad

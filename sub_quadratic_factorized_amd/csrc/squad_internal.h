@@ -160,6 +160,22 @@ hipError_t launch_pass_bf16(const PassGeom& g, int d, const void* q, const void*
 hipError_t launch_pass_f32(const PassGeom& g, int d, const void* q, const void* k,
                            const void* vals, void* out, void* ypad, hipStream_t stream);
 
+// Operands of one pass's backward (unpadded grids).  q, k, vals: the pass's
+// inputs; out: its output O; dout: the upstream gradient dO.  The kernels
+// write dQ and dK (plus addq / addk when those are not null: float32
+// contributions of the other pass) and dV of the values.  In the bf16 kernels
+// q, k, vals, out, dout and dvals are bf16 and dq, dk are float32 when qk_f32,
+// else bf16; in the float32 kernels everything is float32.
+struct BwdArgs {
+    const void *q, *k, *vals, *out, *dout;
+    const float *addq, *addk;
+    void *dq, *dk, *dvals;
+    bool qk_f32;
+};
+
+hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_pass_f32(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 

@@ -29,35 +29,18 @@
 //     it by more than 2^8), so the accumulator rescale is rare and P <= 256.
 #include "squad_internal.h"
 #include "squad_layout.h"
+#include "squad_mfma.h"
 
 #include <mutex>
 
 namespace squad {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 constexpr int BR = kBlockRows;
 constexpr float kRescaleHeadroom = 8.0f;  // log2 units
 
 template <int D>
 using Geo = BlockGeo<D>;
-
-// Maximum over the four lanes {l, l^16, l^32, l^48} that share a query row in
-// the transposed score layout (two half-wave swaps, no LDS traffic).
-__device__ __forceinline__ float row_max4(float x) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-    const uint32_t w = __builtin_bit_cast(uint32_t, y);
-    const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-    return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
-}
 
 // D: head dim; QT: 16-row query tiles per wave; MAXW: waves per workgroup
 // (upper bound, >= NCH/64 so every thread stages exactly one chunk per tensor);

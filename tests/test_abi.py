@@ -161,7 +161,7 @@ def test_flops_and_bytes_helpers():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(8):  # every status the header defines
         assert isinstance(bd.status_str(s), str) and bd.status_str(s)
     assert bd.status_str(123) == "unknown status"
     assert bd.lib().squad_attn_last_hip_error() == 0
@@ -267,3 +267,63 @@ def test_window_solver_matches_oracle_rule():
         bd.squad_window_solve((0, 4, 4))
     with pytest.raises(bd.SquadError):
         bd.squad_window_solve((1 << 11, 1 << 10, 1 << 10))
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+DO, DQ, DK, DV = A + 16 * BYTES, A + 20 * BYTES, A + 24 * BYTES, A + 28 * BYTES
+BWS = A + 32 * BYTES
+BWS_BYTES = 2 * BYTES + 2 * 2 * BYTES  # Y and dY in bf16, float32 dq and dk partials (256-byte rounded: exact here)
+
+
+def bcall(fn="check", q=Q, k=K, v=V, out=O, dout=DO, dq=DQ, dk=DK, dv=DV, ws=BWS, ws_bytes=BWS_BYTES,
+          dtype=bd.SQUAD_BF16, **over):
+    g = dict(GEO)
+    g.update(over)
+    args = (q, k, v, out, dout, dq, dk, dv, ws, ws_bytes, g["B"], g["heads"], g["T"], g["Hs"], g["Ws"], g["wt"],
+            g["wh"], g["ww"], g["d"], dtype)
+    if fn == "check":
+        return bd.squad_attn_check_bwd(*args)
+    return bd.lib().squad_attn_bwd(*args, None)
+
+
+def test_bwd_workspace_and_helpers():
+    assert bd.squad_attn_bwd_workspace_bytes(*GEO.values(), bd.SQUAD_BF16) == BWS_BYTES
+    assert bd.squad_attn_bwd_workspace_bytes(*GEO.values(), bd.SQUAD_F32) == 4 * 2 * BYTES
+    assert bd.squad_attn_bwd_workspace_bytes(*dict(GEO, wh=3).values(), bd.SQUAD_BF16) == -1
+    assert bd.squad_attn_bwd_workspace_bytes(*dict(GEO, B=0).values(), bd.SQUAD_BF16) == 0
+    assert bd.squad_attn_bwd_flops(*GEO.values()) == 2.5 * 63_128_862_720
+    assert bd.squad_attn_bwd_flops(*GEO.values()) == so.squad_backward_flops(*GEO.values())
+    e = 18480 * 24 * 128
+    assert bd.squad_attn_bwd_bytes(*GEO.values(), bd.SQUAD_BF16) == e * 2 * 18 + e * 16
+
+
+@pytest.mark.parametrize("fn", ["check", "bwd"])
+def test_bwd_rejections(fn):
+    assert bcall(fn, wh=3) == bd.SQUAD_ERR_SHAPE
+    assert bcall(fn, d=96) == bd.SQUAD_ERR_UNSUPPORTED
+    for key in ("q", "k", "v", "out", "dout", "dq", "dk", "dv"):
+        assert bcall(fn, **{key: 0}) == bd.SQUAD_ERR_NULL, key
+    assert bcall(fn, ws=0) == bd.SQUAD_ERR_WORKSPACE
+    assert bcall(fn, ws_bytes=BWS_BYTES - 1) == bd.SQUAD_ERR_WORKSPACE
+    assert bcall(fn, dq=0, ws=0) == bd.SQUAD_ERR_NULL
+    for key in ("q", "dout", "dv", "ws"):
+        assert bcall(fn, **{key: {"q": Q, "dout": DO, "dv": DV, "ws": BWS}[key] + 8}) == bd.SQUAD_ERR_ALIGN, key
+    assert bcall(fn, dq=Q) == bd.SQUAD_ERR_ALIAS
+    assert bcall(fn, dk=DO + 16) == bd.SQUAD_ERR_ALIAS
+    assert bcall(fn, dv=O) == bd.SQUAD_ERR_ALIAS
+    assert bcall(fn, dk=DQ) == bd.SQUAD_ERR_ALIAS
+    assert bcall(fn, dv=DK + 32) == bd.SQUAD_ERR_ALIAS
+    assert bcall(fn, ws=V + 16) == bd.SQUAD_ERR_ALIAS
+    assert bcall(fn, dq=BWS + BWS_BYTES - 16) == bd.SQUAD_ERR_ALIAS
+
+
+def test_bwd_check_accepts_what_would_launch():
+    assert bcall() == bd.SQUAD_OK
+    assert bcall(out=Q, dout=K) == bd.SQUAD_OK           # inputs may overlap one another
+    assert bcall(dtype=bd.SQUAD_F32, q=A, k=A + 2 * BYTES, v=A + 4 * BYTES, out=A + 6 * BYTES,
+                 dout=A + 8 * BYTES, dq=A + 10 * BYTES, dk=A + 12 * BYTES, dv=A + 14 * BYTES,
+                 ws=A + 16 * BYTES, ws_bytes=8 * BYTES) == bd.SQUAD_OK
+    assert bcall("bwd", B=0, q=0, k=0, v=0, out=0, dout=0, dq=0, dk=0, dv=0, ws=0) == bd.SQUAD_OK

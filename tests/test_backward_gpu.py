@@ -1,0 +1,112 @@
+"""GPU parity of the backward (squad_attn_bwd through the C ABI) against the
+oracle's gradients on the same seeded inputs and upstream gradient.  `out` is
+the GPU forward's own output, as a caller would pass it."""
+
+import numpy as np
+import pytest
+
+from oracle import squad_oracle as so
+from sub_quadratic_factorized_amd import binding as bd
+from sub_quadratic_factorized_amd import workloads as wl
+
+from gpu_common import errors, host_to_device, log, to_f64, _record
+
+pytestmark = pytest.mark.gpu
+
+# Bars on each gradient's relative L2 error.  float32: as the forward.  bf16:
+# one bf16 rounding (round to nearest even) perturbs a value by about 1.1e-3
+# relative RMS; the gradients pass through about five (Y and dY stored, P or
+# dS entering each MFMA, the forward's O inside D, the stored gradient), which
+# add to ~2.5e-3 in quadrature, and the difference dP - D inside dS = P (dP - D)
+# amplifies that somewhat (~3.5e-3 to 5e-3 expected).  The forward's bar is
+# 5e-3 for half as many roundings; the gradients get twice that.
+F32_GRAD_REL_L2 = 1e-5
+BF16_GRAD_REL_L2 = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bd.lib()
+
+
+def check_grads(got, ref, dtype, what):
+    bar = BF16_GRAD_REL_L2 if dtype == "bf16" else F32_GRAD_REL_L2
+    worst = 0.0
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        max_abs, rel = errors(g, r)
+        log(f"  {what} {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e} max|ref|={np.max(np.abs(r)):.3f}")
+        _record({"case": f"{what} {name}", "dtype": dtype, "max_abs": max_abs, "rel_l2": rel,
+                 "max_ref": float(np.max(np.abs(r)))})
+        worst = max(worst, rel)
+    assert worst <= bar, (what, worst)
+
+
+def run_bwd(geo, dtype, B=1, heads=2, d=64, seed=0):
+    import torch
+    T, Hs, Ws, wt, wh, ww = geo
+    n = T * Hs * Ws
+    log(f"case bwd dtype={dtype} B={B} heads={heads} d={d} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww}")
+    q, k, v = wl.random_geometry_inputs(B, heads, n, d, dtype, seed=seed)
+    do = wl.random_geometry_inputs(B, heads, n, d, dtype, seed=seed + 1000)[0]
+    qd, kd, vd, dod = host_to_device((q, k, v, do), dtype)
+    out = bd.squad_attn_fwd(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww))
+    dq, dk, dv = bd.squad_attn_bwd(qd, kd, vd, out, dod, (T, Hs, Ws), (wt, wh, ww))
+    torch.cuda.synchronize()
+    ref = so.squad_backward(q, k, v, do, (B, heads, T, Hs, Ws, wt, wh, ww, d))
+    check_grads([to_f64(t) for t in (dq, dk, dv)], ref, dtype, f"bwd {geo}")
+
+
+# one block, ragged blocks, several blocks, more query tiles than waves, long
+# windows (m = 336 as the 4x workloads), many windows
+GEOS = [
+    (3, 4, 4, 3, 2, 2),
+    (2, 6, 8, 1, 3, 4),
+    (4, 8, 12, 2, 4, 4),
+    (3, 10, 12, 3, 5, 4),
+    (21, 8, 8, 21, 4, 4),
+    (2, 24, 20, 1, 1, 2),
+]
+
+
+@pytest.mark.parametrize("geo", GEOS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_small(geo, dtype):
+    run_bwd(geo, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_head_dim_128_batch(dtype):
+    run_bwd((3, 8, 10, 3, 2, 5), dtype, B=2, heads=3, d=128, seed=4)
+
+
+def test_backward_headline_sampled_heads():
+    import torch
+    w = wl.WORKLOADS["wan5b_704p"]
+    log("case bwd workload=wan5b_704p (generating inputs)")
+    qd, kd, vd = wl.device_inputs(w, seed=0)
+    dod = wl.device_inputs(w, seed=1)[0]
+    grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)
+    out = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    dq, dk, dv = bd.squad_attn_bwd(qd, kd, vd, out, dod, grid, window)
+    torch.cuda.synchronize()
+    table = so.window_slot_table(*grid, *window)
+    for h in (0, 17):
+        q, k, v = wl.head_slices_f64(w, 0, h)
+        do = to_f64(dod[0, :, h, :])
+        ref = so.squad_backward_head(q, k, v, do, table)
+        check_grads([to_f64(t[0, :, h, :]) for t in (dq, dk, dv)], ref, "bf16", f"wan5b_704p h={h}")
+
+
+def test_backward_deterministic():
+    import torch
+    geo = (2, 6, 8, 1, 3, 4)
+    q, k, v = wl.random_geometry_inputs(1, 2, 96, 64, "bf16", seed=9)
+    qd, kd, vd = host_to_device((q, k, v), "bf16")
+    out = bd.squad_attn_fwd(qd, kd, vd, geo[:3], geo[3:])
+    a = bd.squad_attn_bwd(qd, kd, vd, out, vd, geo[:3], geo[3:])
+    b = bd.squad_attn_bwd(qd, kd, vd, out, vd, geo[:3], geo[3:])
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
