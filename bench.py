@@ -411,6 +411,24 @@ def main():
         "baseline_context": {"pages_ms_per_block": PAGES_MS_PER_BLOCK, "hardware": "NVIDIA H100 80GB (pages)"},
         "kernel_source_hash": kernel_source_hash(),
     }
+    # ---- the gradients of the same call (squad_attn_bwd), same inputs ---------
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dout = wl.device_inputs(w, seed=1)[0]
+    ws = torch.empty(bd.squad_attn_bwd_workspace_bytes(*w.geometry(), dt), dtype=torch.uint8, device="cuda")
+
+    def bwd(s):
+        bd.squad_attn_bwd(s[0], s[1], s[2], s[3], dout, grid, window, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    bwd_ms = time_loop(bwd, max(args.kernel_iters // 5, 5), sets)
+    bwd_flops = bd.squad_attn_bwd_flops(*w.geometry())
+    bwd_bytes = bd.squad_attn_bwd_bytes(*w.geometry(), dt)
+    eprint(f"[bench] backward {bwd_ms:.4f} ms ({bwd_flops / (bwd_ms * 1e-3) / 1e12:.1f} TFLOP/s)")
+    out["backward"] = {"ms": bwd_ms, "tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12, "flops": bwd_flops,
+                       "kernel_bytes": bwd_bytes, "gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
+                       "mfma_peak_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                       "hbm_peak_frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del dq, dk, dv, dout, ws
+
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
         src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
