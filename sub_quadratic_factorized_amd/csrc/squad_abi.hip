@@ -190,6 +190,10 @@ PassGeom make_geom(const Problem& pr, bool global) {
     g.ww = pr.ww;
     g.Cy = Hp / pr.wh;
     g.Cx = Wp / pr.ww;
+    g.parts = 1;
+    g.part_tiles = (g.L + 15) / 16;
+    g.nitems = g.nprob;
+    g.div_parts = make_fastdiv(1);
     g.pad = padded ? 1 : 0;
     g.Hp = Hp;
     g.Wp = Wp;

@@ -63,6 +63,14 @@ struct PassGeom {
     // packed padded coordinates (see pack_coords) instead of a token offset.
     // The local outputs of padded tokens live in a side buffer of npad tokens
     // per batch element ([B, npad, heads, d]).
+    // Long problems may be split by query rows into `parts` work items of
+    // part_tiles 16-row query tiles (the last may have fewer); each item
+    // streams all the problem's keys and values.  Items of one problem are 8
+    // apart (nitems = nprob * parts; splitting needs nprob % 8 == 0 and a pass
+    // that is not in place).  Only the bf16 forward splits; everything else
+    // has parts = 1.
+    int parts, part_tiles, nitems;
+    FastDiv div_parts;
     int pad;
     int Hp, Wp;
     int pad_per_frame;  // Hs*(Wp - Ws) + (Hp - Hs)*Wp padded tokens per frame

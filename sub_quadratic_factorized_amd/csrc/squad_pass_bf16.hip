@@ -48,11 +48,16 @@ using Geo = BlockGeo<D>;
 // for; LMAX: longest problem of this instance (sizes the LDS Q stage); QSTAGE:
 // stream Q through the LDS stage (else each wave loads its Q tiles straight
 // into registers at a problem's first step, for problems too long to stage).
+// A work item is a problem or, for long problems (PassGeom::parts > 1), one
+// part of its query rows; the item streams all of the problem's keys and
+// values either way.
 // GP: the global pass (rows of a problem are windows at one slot) rather than
 // the local pass (rows are the slots of one window).  PAD: a padded grid (rows
 // named by packed padded coordinates; q, k and the local pass's values read
-// through mirror images; padded rows of Y in the side buffer yp).
-template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD>
+// through mirror images; padded rows of Y in the side buffer yp).  SPLIT:
+// items are parts of problems (PassGeom::parts > 1); otherwise items are
+// whole problems and the part logic compiles away.
+template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT>
 __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __restrict__ qp,
                                           const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
                                           uint16_t* yp, float scale_log2) {
@@ -62,7 +67,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][BR * G::KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][BR * G::VSTR];
     __shared__ __attribute__((aligned(16))) uint16_t qstage[QROWS * G::KSTR];
-    __shared__ int tab[LMAX];
+    __shared__ int tab[kMaxLen];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -70,12 +75,10 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     const int li = lane & 15;
     const int lg = lane >> 4;
     const int L = g.L;
-    const int NB = (L + BR - 1) / BR;
-    const int ntiles = (L + 15) / 16;
-    // waves past the last tile only stage data; a wave's partial tiles compute
-    // on clamped rows and are never stored
-    const bool computes = wave * QT < ntiles;
-    const int nmine = (g.nprob - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int NB = (L + BR - 1) / BR;  // key / value blocks of a problem
+    // rows of the Q stage filled per item (all of a problem's, or of a part's)
+    constexpr int QCAP = QSTAGE ? (LMAX + BR - 1) / BR * BR : 0;
+    const int nmine = (g.nitems - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
     const int total = nmine * NB;  // steps
     const int row_stride = g.heads * D;
     const bool ragged = NB * BR != L;
@@ -91,21 +94,31 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         tab[r] = PAD ? (GP ? win_coords(g, r) : slot_coords(g, r)) : (GP ? win_origin(g, r) : slot_offset(g, r));
     __syncthreads();
 
-    // A problem: unpadded, the offset of its base token's row (row r adds
-    // tab[r] * row_stride); padded, the (b, h) offsets into the tensors and
-    // into the side buffer, and its packed base coordinates.
+    // A work item: unpadded, the offset of its problem's base token row (row
+    // r adds tab[r] * row_stride); padded, the (b, h) offsets into the tensors
+    // and into the side buffer, and the packed base coordinates; and its query
+    // rows q0 .. q0 + qn - 1 of the problem.
     struct Prob {
         int64_t off, yoff;
-        int base;
+        int base, q0, qn;
     };
     auto problem = [&](int it) -> Prob {
-        const ProblemIndex pr = decode_problem(g, (int)blockIdx.x + it * (int)gridDim.x);
+        int p = (int)blockIdx.x + it * (int)gridDim.x, part = 0;
+        if (SPLIT) {  // item 8 (c * parts + part) + x -> problem 8 c + x
+            const int y = p >> 3;
+            const int c = (int)fdiv((uint32_t)y, g.div_parts);
+            part = y - c * g.parts;
+            p = c * 8 + (p & 7);
+        }
+        const int q0 = SPLIT ? part * g.part_tiles * 16 : 0;
+        const int qn = SPLIT ? min(L - q0, g.part_tiles * 16) : L;
+        const ProblemIndex pr = decode_problem(g, p);
         if (PAD)
             return Prob{(int64_t)pr.b * g.n * row_stride + (int64_t)pr.h * D,
                         (int64_t)pr.b * g.npad * row_stride + (int64_t)pr.h * D,
-                        GP ? slot_coords(g, pr.pi) : win_coords(g, pr.pi)};
+                        GP ? slot_coords(g, pr.pi) : win_coords(g, pr.pi), q0, qn};
         const int base = GP ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
-        return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0};
+        return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0, q0, qn};
     };
     // offset, in q, k and the local pass's values, of the row with table entry tv
     auto src_off = [&](const Prob& pr, int tv) -> int64_t {
@@ -114,18 +127,19 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     };
 
     // ---- loader -------------------------------------------------------------
-    // Step (it, b) stages K and V rows of block b of problem it and Q rows of
-    // block b of problem it+1.  Past-the-end rows are clamped to the last row
-    // (their scores are masked, their probabilities zero, their outputs never
-    // stored) and past-the-end problems to the last one (never consumed).
+    // Step (it, b) stages K and V rows of block b of item it and Q rows of
+    // block b of item it+1's query rows.  Past-the-end rows are clamped to
+    // the last row (their scores are masked, their probabilities zero, their
+    // outputs never stored); Q blocks past an item's query rows read a dead
+    // address.
     u32x4 sk[PD], sv[PD], sq[PD];
     int ld_it = 0, ld_b = 0;
     // loads of steps past the last problem, and of Q past the last problem,
     // all read the first 16 bytes of the tensor (one cached line, never used)
     bool ld_dead = nmine <= 0;
     bool q_dead = nmine <= 1;
-    Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0};
-    Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0};
+    Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0, 0, 1};
+    Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0, 0, 1};
 
     auto issue = [&](u32x4& dk, u32x4& dv, u32x4& dq) {
         const int tv = tab[min(ld_b * BR + ld_row, L - 1)];
@@ -140,7 +154,12 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         }
         dk = *reinterpret_cast<const u32x4*>(kp + (ld_dead ? 0 : a));
         dv = *reinterpret_cast<const u32x4*>(vb + (ld_dead ? 0 : av));
-        if (QSTAGE) dq = *reinterpret_cast<const u32x4*>(qp + (q_dead ? 0 : src_off(ld_q, tv) + ld_col));
+        if (QSTAGE) {
+            // row of the next item's query rows (unsplit: the key / value row)
+            const int tq = SPLIT ? tab[ld_q.q0 + min(ld_b * BR + ld_row, ld_q.qn - 1)] : tv;
+            const bool qd = q_dead || (SPLIT && ld_b * BR >= ld_q.qn);
+            dq = *reinterpret_cast<const u32x4*>(qp + (qd ? 0 : src_off(ld_q, tq) + ld_col));
+        }
         if (++ld_b == NB) {
             ld_b = 0;
             ++ld_it;
@@ -160,7 +179,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         if (stager) {
             *reinterpret_cast<u32x4*>(&kbuf[buf][ld_row * G::KSTR + ld_col]) = dk;
             *reinterpret_cast<u32x4*>(&vbuf[buf][v_put]) = v_swap ? u32x4{dv.z, dv.w, dv.x, dv.y} : dv;
-            if (QSTAGE) *reinterpret_cast<u32x4*>(&qstage[(blk * BR + ld_row) * G::KSTR + ld_col]) = dq;
+            if (QSTAGE && (!SPLIT || blk * BR < QCAP))
+                *reinterpret_cast<u32x4*>(&qstage[(blk * BR + ld_row) * G::KSTR + ld_col]) = dq;
         }
     };
 
@@ -170,15 +190,19 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     f32x4 osum[QT];  // every row: running sum of P for the lane's query
     bf16x8 pk[QT];
     float mrun[QT];
-    Prob cur_p{0, 0, 0};
+    Prob cur_p{0, 0, 0, 0, 1};
     int c_it = 0;
+    // waves past the item's last query tile only stage data; a wave's partial
+    // tiles compute on clamped rows and are never stored (unsplit: the same
+    // for every item)
+    bool computes = wave * QT * 16 < L;
 
     const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
     // Q tiles of this wave (from the LDS stage, or straight from memory) into
     // MFMA B-operand registers
     auto read_q = [&]() {
-        const Prob qprob = QSTAGE ? Prob{0, 0, 0} : problem(c_it);
+        const Prob qprob = QSTAGE ? Prob{0, 0, 0, 0, 1} : problem(c_it);
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             const int row = (wave * QT + t) * 16 + li;
@@ -187,7 +211,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                 if (QSTAGE) {
                     qreg[t][s] = *reinterpret_cast<const bf16x8*>(&qstage[row * G::KSTR + (4 * s + lg) * 8]);
                 } else {
-                    const int64_t a = src_off(qprob, tab[min(row, L - 1)]) + (4 * s + lg) * 8;
+                    const int64_t a = src_off(qprob, tab[qprob.q0 + min(row, qprob.qn - 1)]) + (4 * s + lg) * 8;
                     qreg[t][s] = *reinterpret_cast<const bf16x8*>(qp + a);
                 }
             }
@@ -196,6 +220,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 
     auto start_problem = [&]() {
         cur_p = problem(c_it);
+        if (SPLIT) computes = wave * QT * 16 < cur_p.qn;
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             mrun[t] = -INFINITY;
@@ -300,10 +325,10 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             const int row = (wave * QT + t) * 16 + li;
             // padded grids: real rows to out, padded rows of the local pass to
             // the side buffer, padded rows of the global pass nowhere (cropped)
-            bool keep = row < L;
+            bool keep = row < cur_p.qn;
             uint16_t* dst = op;
             if (keep) {
-                const int tv = tab[row];
+                const int tv = tab[cur_p.q0 + row];
                 if (!PAD) {
                     dst = op + cur_p.off + (int64_t)tv * row_stride + 8 * lg;
                 } else if (is_real(g, cur_p.base + tv)) {
@@ -331,8 +356,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // prologue: Q of the first problem straight into the stage, then PD steps in flight
     if (QSTAGE && nmine > 0) {
         const Prob p0 = problem(0);
-        for (int r = wave; r < NB * BR; r += blockDim.x >> 6) {
-            const int64_t a = src_off(p0, tab[min(r, L - 1)]);
+        for (int r = wave; r < QCAP; r += blockDim.x >> 6) {
+            const int64_t a = src_off(p0, tab[p0.q0 + min(r, p0.qn - 1)]);
             for (int c = lane; c < G::KC; c += 64)
                 *reinterpret_cast<u32x4*>(&qstage[r * G::KSTR + c * 8]) =
                     *reinterpret_cast<const u32x4*>(qp + a + c * 8);
@@ -380,18 +405,18 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 }
 
 // The two passes as distinct kernels (so profiles tell them apart).
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_local_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD>(g, qp, kp, vp, op, yp, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT>(g, qp, kp, vp, op, yp, scale_log2);
 }
 
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_global_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD>(g, qp, kp, vp, op, yp, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT>(g, qp, kp, vp, op, yp, scale_log2);
 }
 
 int grid_for(const void* kern, int threads, int nprob) {
@@ -424,17 +449,27 @@ int grid_for(const void* kern, int threads, int nprob) {
 // the waves of one workgroup; a workgroup has at least NCH/64 waves (8 at
 // d = 128, 4 at d = 64) so that every thread stages one chunk per tensor.  The
 // register budget follows the waves that share a SIMD (<= 12 waves: 168
-// VGPRs; 8 waves: 256); longer problems put 2, 3 or 4 tiles on each wave.
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD>
+// VGPRs; 8 waves: 256).  Problems of up to 12 tiles run one tile per wave.
+// Longer ones are split into 2 or 3 parts of query rows (items) run by that
+// same instance when the problem count is a multiple of 8 and the pass is
+// not in place (a part writes its rows of `out` while another part of the
+// problem may still be reading them as values otherwise): the parts of a
+// problem are 8 items apart and the grid is a multiple of 8 * parts, so they
+// run in the same round on workgroups 8 apart, which round-robin dispatch puts
+// on the same XCD, and their repeated key / value reads are served by its L2.
+// Otherwise 2, 3 or 4 tiles go on each wave.
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT = false>
 hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o, void* y,
                       hipStream_t st) {
-    auto kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD>
-                        : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD>;
+    auto kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>
+                        : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>;
     const void* kern = reinterpret_cast<const void*>(kfn);
     const int threads = 64 * waves;
-    if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.L > LMAX || (g.L + 15) / 16 > QT * waves)
+    if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.part_tiles * 16 > LMAX || g.part_tiles > QT * waves ||
+        (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0))
         return hipErrorInvalidConfiguration;  // the menu never asks for this
-    const int grid = grid_for(kern, threads, g.nprob);
+    int grid = grid_for(kern, threads, g.nitems);
+    if (g.parts > 1 && grid >= 8 * g.parts) grid -= grid % (8 * g.parts);
     const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf((float)D);
     hipLaunchKernelGGL(kfn, dim3(grid), dim3(threads), 0, st, g, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
@@ -443,12 +478,20 @@ hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k
 }
 
 template <int D, bool PAD>
-hipError_t launch_d(const PassGeom& g, const void* q, const void* k, const void* v, void* o, void* y,
+hipError_t launch_d(const PassGeom& g0, const void* q, const void* k, const void* v, void* o, void* y,
                     hipStream_t st) {
     constexpr int minw = Geo<D>::NCH / 64;
-    const int tiles = (g.L + 15) / 16;
-    if (tiles <= 12)
-        return launch_one<D, 1, 12, 4, 3, 192, true, PAD>(g, tiles > minw ? tiles : minw, q, k, v, o, y, st);
+    const int tiles = (g0.L + 15) / 16;
+    PassGeom g = g0;
+    if (tiles > 12 && g.nprob % 8 == 0 && v != o) {
+        g.parts = (tiles + 11) / 12;
+        g.part_tiles = (tiles + g.parts - 1) / g.parts;
+        g.nitems = g.nprob * g.parts;
+        g.div_parts = make_fastdiv((uint32_t)g.parts);
+    }
+    const int waves = g.part_tiles > minw ? g.part_tiles : minw;
+    if (g.parts > 1) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, true>(g, waves, q, k, v, o, y, st);
+    if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true, PAD>(g, waves, q, k, v, o, y, st);
     if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD>(g, 8, q, k, v, o, y, st);
     if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD>(g, 8, q, k, v, o, y, st);
     return launch_one<D, 4, 8, 2, 2, 512, false, PAD>(g, 8, q, k, v, o, y, st);

@@ -124,3 +124,8 @@ def test_solved_windows_run():
     for grid in [(21, 6, 11), (21, 8, 14), (5, 9, 16)]:
         win = bd.squad_window_solve(grid)
         run_padded(grid + win, "bf16", heads=2, d=128, seed=sum(grid))
+
+
+def test_padded_split_long_windows():
+    # m = 315 with 4 heads: 440 local problems, split into two query parts
+    run_padded((21, 30, 52, 21, 3, 5), "bf16", heads=4, d=128, seed=11)

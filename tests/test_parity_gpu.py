@@ -243,3 +243,44 @@ def test_rejections_raise():
 def test_many_heads_small_dim(dtype, op):
     # 32 heads at d=64: 64 windows x 64 slots per head, row stride 2048
     run_small((4, 32, 32, 4, 4, 4), dtype, op, heads=32, d=64)
+
+
+# ---------------------------------------------------------------------------
+# Long problems split into query parts (problem count a multiple of 8)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("geo,heads", [
+    ((21, 8, 8, 21, 4, 4), 8),     # m = 336: 2 parts of 11 + 10 tiles, 32 local problems
+    ((5, 10, 16, 5, 5, 8), 2),     # m = 200: 7 + 6 tiles, ragged last block
+    ((5, 16, 10, 5, 8, 10), 4),    # m = 400: 3 parts of 9 + 9 + 7 tiles
+    ((8, 8, 16, 8, 8, 8), 4),      # m = 512: 3 parts of 11 + 11 + 10 tiles
+])
+@pytest.mark.parametrize("op", ["fwd", "local"])
+def test_split_long_problems(geo, heads, op):
+    run_small(geo, "bf16", op, heads=heads, d=128, seed=17)
+
+
+def test_split_long_problems_head_dim_64():
+    run_small((21, 8, 8, 21, 4, 4), "bf16", "local", heads=8, d=64, seed=18)
+
+
+def test_split_many_slots_global():
+    # global pass over N_w = 200 windows at each of 8 slots x 2 heads (16 problems)
+    run_small((2, 20, 80, 1, 2, 4), "bf16", "global", heads=2, d=64, seed=19)
+
+
+@pytest.mark.parametrize("fn", ["local", "global", "fwd", "reversed"])
+def test_in_place_long_problems_against_oracle(fn):
+    # lengths that split when not in place (m = 336 local, N_w = 400 global,
+    # problem counts multiples of 8): in place every pass must stay whole
+    import torch
+    for geo, heads, d in (((21, 8, 8, 21, 4, 4), 8, 64), ((2, 20, 80, 1, 2, 4), 2, 64)):
+        T, Hs, Ws, wt, wh, ww = geo
+        log(f"case in-place {fn} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} heads={heads}")
+        q, k, v = wl.random_geometry_inputs(1, heads, T * Hs * Ws, d, "bf16", seed=23)
+        qd, kd, vd = host_to_device((q, k, v), "bf16")
+        gpu_fn, ref_fn = OPS[fn]
+        buf = vd.clone()
+        gpu_fn(qd, kd, buf, (T, Hs, Ws), (wt, wh, ww), out=buf)
+        torch.cuda.synchronize()
+        assert_close(to_f64(buf), ref_fn(q, k, v, (1, heads, T, Hs, Ws, wt, wh, ww, d)), "bf16", f"in place {fn}")
