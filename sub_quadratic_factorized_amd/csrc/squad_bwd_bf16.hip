@@ -7,8 +7,13 @@
 //     dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
 //
 // One workgroup of 8 waves per problem; rows stream through LDS in blocks of
-// 32 (clamped past the end, masked).  Two kinds of MFMA product occur, both
-// on v_mfma_f32_16x16x32_bf16 with the operand layouts of the forward kernel:
+// 32 (clamped past the end, masked) along one sequence of steps: per group of
+// query tiles, NB steps over K then NB over K and V; per group of key tiles,
+// NB steps over Q and dO.  Every thread stages one 16-byte chunk of each of
+// the step's (up to) two tensors in registers PD steps ahead of use, with
+// unconditional loads, into double-buffered LDS, one barrier per step.  Two
+// kinds of MFMA product occur, both on v_mfma_f32_16x16x32_bf16 with the
+// operand layouts of the forward kernel:
 //   * over d (S, dP): both operands are token rows, read as 16-byte row
 //     chunks (the K/Q row layout in LDS, or registers loaded from memory);
 //   * over tokens (dQ^T = K^T dS^T, dV^T = dO^T P, dK^T = Q^T dS): the A
@@ -30,6 +35,7 @@ namespace {
 
 constexpr int BR = kBlockRows;
 constexpr int NW = 8;  // waves per workgroup
+constexpr int PD = 2;  // steps in flight
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -52,10 +58,10 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     const float* __restrict__ addk, void* __restrict__ dqp, void* __restrict__ dkp, uint16_t* __restrict__ dvp,
     int qk_f32, float c_log2, float scale) {
     using G = BlockGeo<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t rowA[BR * G::KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t rowB[BR * G::KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t trA[BR * G::VSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t trB[BR * G::VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t rowA[2][BR * G::KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t rowB[2][BR * G::KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t trA[2][BR * G::VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t trB[2][BR * G::VSTR];
     __shared__ float lse[kMaxLen], dd[kMaxLen];
     __shared__ int tab[kMaxLen];
 
@@ -78,16 +84,43 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     // element offset of row r of the problem (rows past the end clamped)
     auto row = [&](int r) -> int64_t { return bh + (int64_t)(base + tab[min(r, L - 1)]) * row_stride; };
 
-    // rows blk*32 .. +31 of x into the row layout and / or the transposed-read layout
-    auto stage = [&](const uint16_t* x, int blk, uint16_t* rb, uint16_t* tb) {
-        for (int c = tid; c < G::NCH; c += 64 * NW) {
-            const int r = c / G::KC, col = (c % G::KC) * 8;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(x + row(blk * BR + r) + col);
-            if (rb) *reinterpret_cast<u32x4*>(&rb[r * G::KSTR + col]) = v;
-            if (tb)
-                *reinterpret_cast<u32x4*>(&tb[v_chunk_offset<D>(r, col / 8)]) =
-                    v_halves_swapped<D>(r) ? u32x4{v.z, v.w, v.x, v.y} : v;
+    // ---- loader ---------------------------------------------------------------
+    // Step kinds: the log-sum-exp pass over K (K -> row layout), the dQ pass
+    // over K and V (K -> row and transposed layouts, V -> row layout), the
+    // dK / dV pass over Q and dO (both -> row and transposed layouts).
+    enum { kLse = 0, kDq = 1, kDkv = 2 };
+    const int nsteps_a = ngroups * 2 * NB;  // even: sweep B starts on slot 0
+    const int nsteps = nsteps_a + ngroups * NB;
+    const bool stager = tid < G::NCH;
+    const int ch = stager ? tid : G::NCH - 1;
+    const int ld_row = ch / G::KC;
+    const int ld_col = (ch % G::KC) * 8;
+    int ld_s = 0, ld_blk = 0, ld_kind = kLse;
+    u32x4 sx1[PD], sx2[PD];
+    auto issue = [&](u32x4& x1, u32x4& x2) {
+        const bool dead = ld_s >= nsteps;
+        const int64_t a = row(ld_blk * BR + ld_row) + ld_col;
+        const uint16_t* p1 = ld_kind == kDkv ? qp : kp;
+        const uint16_t* p2 = ld_kind == kDkv ? dop : vp;
+        x1 = *reinterpret_cast<const u32x4*>(p1 + (dead ? 0 : a));
+        x2 = *reinterpret_cast<const u32x4*>(p2 + (dead || ld_kind == kLse ? 0 : a));
+        ++ld_s;
+        if (++ld_blk == NB) {
+            ld_blk = 0;
+            ld_kind = ld_s >= nsteps_a ? kDkv : (ld_kind == kLse ? kDq : kLse);
         }
+    };
+    const int t_put = v_chunk_offset<D>(ld_row, ld_col / 8);
+    const bool t_swap = v_halves_swapped<D>(ld_row);
+    auto put = [&](const u32x4& x1, const u32x4& x2, int buf, int kind) {
+        if (!stager) return;
+        *reinterpret_cast<u32x4*>(&rowA[buf][ld_row * G::KSTR + ld_col]) = x1;
+        if (kind != kLse) {
+            *reinterpret_cast<u32x4*>(&trA[buf][t_put]) = t_swap ? u32x4{x1.z, x1.w, x1.x, x1.y} : x1;
+            *reinterpret_cast<u32x4*>(&rowB[buf][ld_row * G::KSTR + ld_col]) = x2;
+        }
+        if (kind == kDkv)
+            *reinterpret_cast<u32x4*>(&trB[buf][t_put]) = t_swap ? u32x4{x2.z, x2.w, x2.x, x2.y} : x2;
     };
     // a 16-row tile of x as the row operand (lane: row li, d = 32s + 8lg ..)
     auto load_tile = [&](const uint16_t* x, int tile, bf16x8 (&reg)[G::KS]) {
@@ -144,144 +177,150 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     };
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    // ---- query sweep: log-sum-exp, D, dQ ------------------------------------
-    for (int grp = 0; grp < ngroups; ++grp) {
-        const int qt = grp * NW + wave;
-        const bool active = qt < ntiles;
-        bf16x8 qreg[G::KS], doreg[G::KS];
-        float Dq = 0.0f;
-        if (active) {
-            load_tile(qp, qt, qreg);
-            load_tile(dop, qt, doreg);
-            const int64_t a = row(qt * 16 + li);
-            float part = 0.0f;
 #pragma unroll
-            for (int s = 0; s < G::KS; ++s) {
-                const bf16x8 o = *reinterpret_cast<const bf16x8*>(op + a + (4 * s + lg) * 8);
+    for (int u = 0; u < PD; ++u) issue(sx1[u], sx2[u]);
+
+    // ---- sweep A: per query group, log-sum-exp over K then dQ over K and V ----
+    bf16x8 qreg[G::KS], doreg[G::KS];
+    float Dq = 0.0f, m = -INFINITY, l = 0.0f, lse2 = 0.0f;
+    f32x4 dqacc[G::DT];
+    int st = 0;  // step of sweep A
+    for (int s0 = 0; s0 < nsteps_a; s0 += PD) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[s][e], (float)o[e], part);
-            }
-            Dq = row_sum4(part);
-        }
-        // scores S^T (keys x this wave's queries): row maximum and sum of exp2
-        float m = -INFINITY, l = 0.0f;
-        for (int kb = 0; kb < NB; ++kb) {
-            __syncthreads();
-            stage(kp, kb, rowA, nullptr);
-            __syncthreads();
-            if (active) {
-                f32x4 s0 = zero, s1 = zero;
+        for (int u = 0; u < PD; ++u, ++st) {
+            const int grp = st / (2 * NB), r = st - grp * 2 * NB;
+            const int kind = r < NB ? kLse : kDq, blk = r < NB ? r : r - NB;
+            const int qt = grp * NW + wave;
+            const bool active = qt < ntiles;
+            put(sx1[u], sx2[u], u, kind);
+            issue(sx1[u], sx2[u]);
+            if (kind == kLse && blk == 0 && active) {
+                load_tile(qp, qt, qreg);
+                load_tile(dop, qt, doreg);
+                const int64_t a = row(qt * 16 + li);
+                float part = 0.0f;
 #pragma unroll
                 for (int s = 0; s < G::KS; ++s) {
-                    s0 = mfma(row_op(rowA, 0, s), qreg[s], s0);
-                    s1 = mfma(row_op(rowA, 1, s), qreg[s], s1);
+                    const bf16x8 o = *reinterpret_cast<const bf16x8*>(op + a + (4 * s + lg) * 8);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[s][e], (float)o[e], part);
+                }
+                Dq = row_sum4(part);
+                m = -INFINITY;
+                l = 0.0f;
+            }
+            __syncthreads();
+            if (!active) continue;
+            if (kind == kLse) {
+                // scores S^T (keys x this wave's queries): row maximum and sum of exp2
+                f32x4 sa = zero, sb = zero;
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    sa = mfma(row_op(rowA[u], 0, s), qreg[s], sa);
+                    sb = mfma(row_op(rowA[u], 1, s), qreg[s], sb);
                 }
                 float mx = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    if (kb * BR + 4 * lg + i >= L) s0[i] = -INFINITY;
-                    if (kb * BR + 16 + 4 * lg + i >= L) s1[i] = -INFINITY;
-                    mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+                    if (blk * BR + 4 * lg + i >= L) sa[i] = -INFINITY;
+                    if (blk * BR + 16 + 4 * lg + i >= L) sb[i] = -INFINITY;
+                    mx = fmaxf(mx, fmaxf(sa[i], sb[i]));
                 }
                 const float mnew = fmaxf(m, row_max4(mx) * c_log2);
                 float part = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    part += __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -mnew)) +
-                            __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -mnew));
+                    part += __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -mnew)) +
+                            __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -mnew));
                 l = l * __builtin_amdgcn_exp2f(m - mnew) + row_sum4(part);
                 m = mnew;
-            }
-        }
-        const float lse2 = m + __builtin_log2f(l);
-        if (active && lg == 0 && qt * 16 + li < L) {
-            lse[qt * 16 + li] = lse2;
-            dd[qt * 16 + li] = Dq;
-        }
-        // dQ^T += K^T dS^T over key blocks
-        f32x4 dqacc[G::DT];
+                if (blk == NB - 1) {
+                    lse2 = m + __builtin_log2f(l);
+                    if (lg == 0 && qt * 16 + li < L) {
+                        lse[qt * 16 + li] = lse2;
+                        dd[qt * 16 + li] = Dq;
+                    }
 #pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
-        for (int kb = 0; kb < NB; ++kb) {
-            __syncthreads();
-            stage(kp, kb, rowA, trA);
-            stage(vp, kb, rowB, nullptr);
-            __syncthreads();
-            if (active) {
-                f32x4 s0 = zero, s1 = zero, p0 = zero, p1 = zero;
+                    for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
+                }
+            } else {
+                // dQ^T += K^T dS^T
+                f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
 #pragma unroll
                 for (int s = 0; s < G::KS; ++s) {
-                    s0 = mfma(row_op(rowA, 0, s), qreg[s], s0);
-                    s1 = mfma(row_op(rowA, 1, s), qreg[s], s1);
-                    p0 = mfma(row_op(rowB, 0, s), doreg[s], p0);  // dP^T
-                    p1 = mfma(row_op(rowB, 1, s), doreg[s], p1);
+                    sa = mfma(row_op(rowA[u], 0, s), qreg[s], sa);
+                    sb = mfma(row_op(rowA[u], 1, s), qreg[s], sb);
+                    pa = mfma(row_op(rowB[u], 0, s), doreg[s], pa);  // dP^T
+                    pb = mfma(row_op(rowB[u], 1, s), doreg[s], pb);
                 }
                 float ds0[4], ds1[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool v0 = kb * BR + 4 * lg + i < L, v1 = kb * BR + 16 + 4 * lg + i < L;
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -lse2));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -lse2));
-                    ds0[i] = v0 ? e0 * (p0[i] - Dq) : 0.0f;
-                    ds1[i] = v1 ? e1 * (p1[i] - Dq) : 0.0f;
+                    const bool v0 = blk * BR + 4 * lg + i < L, v1 = blk * BR + 16 + 4 * lg + i < L;
+                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -lse2));
+                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -lse2));
+                    ds0[i] = v0 ? e0 * (pa[i] - Dq) : 0.0f;
+                    ds1[i] = v1 ? e1 * (pb[i] - Dq) : 0.0f;
                 }
                 const bf16x8 dsk = pack8(ds0, ds1);
 #pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = mfma(tr_op(trA, dt), dsk, dqacc[dt]);
+                for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = mfma(tr_op(trA[u], dt), dsk, dqacc[dt]);
+                if (blk == NB - 1) store_rows(dqacc, scale, qt, addq, dqp, qk_f32 != 0);
             }
         }
-        if (active) store_rows(dqacc, scale, qt, addq, dqp, qk_f32 != 0);
     }
-    __syncthreads();  // every row's log-sum-exp and D are in LDS
 
-    // ---- key sweep: dV, dK ---------------------------------------------------
-    for (int grp = 0; grp < ngroups; ++grp) {
-        const int kt = grp * NW + wave;
-        const bool active = kt < ntiles;
-        bf16x8 kreg[G::KS], vreg[G::KS];
-        if (active) {
-            load_tile(kp, kt, kreg);
-            load_tile(vp, kt, vreg);
-        }
-        f32x4 dkacc[G::DT], dvacc[G::DT];
+    // ---- sweep B: per key group, dV and dK over Q and dO --------------------
+    // (every row's log-sum-exp and D reached LDS before the barriers since)
+    bf16x8 kreg[G::KS], vreg[G::KS];
+    f32x4 dkacc[G::DT], dvacc[G::DT];
+    st = 0;  // step of sweep B
+    for (int s0 = nsteps_a; s0 < nsteps; s0 += PD) {
 #pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt) dkacc[dt] = dvacc[dt] = zero;
-        for (int qb = 0; qb < NB; ++qb) {
-            __syncthreads();
-            stage(qp, qb, rowA, trA);
-            stage(dop, qb, rowB, trB);
-            __syncthreads();
-            if (active) {
-                f32x4 s0 = zero, s1 = zero, p0 = zero, p1 = zero;
+        for (int u = 0; u < PD; ++u, ++st) {
+            const bool live = nsteps_a + st < nsteps;
+            const int grp = st / NB, qb = st - grp * NB;
+            const int kt = grp * NW + wave;
+            const bool active = live && kt < ntiles;
+            put(sx1[u], sx2[u], u, kDkv);
+            issue(sx1[u], sx2[u]);
+            if (active && qb == 0) {
+                load_tile(kp, kt, kreg);
+                load_tile(vp, kt, vreg);
 #pragma unroll
-                for (int s = 0; s < G::KS; ++s) {
-                    s0 = mfma(row_op(rowA, 0, s), kreg[s], s0);  // S (queries x this wave's keys)
-                    s1 = mfma(row_op(rowA, 1, s), kreg[s], s1);
-                    p0 = mfma(row_op(rowB, 0, s), vreg[s], p0);  // dP
-                    p1 = mfma(row_op(rowB, 1, s), vreg[s], p1);
-                }
-                float pr0[4], pr1[4], ds0[4], ds1[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int q0 = qb * BR + 4 * lg + i, q1 = q0 + 16;
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(s0[i], c_log2, -lse[q0]));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(s1[i], c_log2, -lse[q1]));
-                    pr0[i] = q0 < L ? e0 : 0.0f;
-                    pr1[i] = q1 < L ? e1 : 0.0f;
-                    ds0[i] = q0 < L ? e0 * (p0[i] - dd[q0]) : 0.0f;
-                    ds1[i] = q1 < L ? e1 * (p1[i] - dd[q1]) : 0.0f;
-                }
-                const bf16x8 pp = pack8(pr0, pr1), dsp = pack8(ds0, ds1);
-#pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt) {
-                    dvacc[dt] = mfma(tr_op(trB, dt), pp, dvacc[dt]);
-                    dkacc[dt] = mfma(tr_op(trA, dt), dsp, dkacc[dt]);
-                }
+                for (int dt = 0; dt < G::DT; ++dt) dkacc[dt] = dvacc[dt] = zero;
             }
-        }
-        if (active) {
-            store_rows(dkacc, scale, kt, addk, dkp, qk_f32 != 0);
-            store_rows(dvacc, 1.0f, kt, nullptr, dvp, false);
+            __syncthreads();
+            if (!active) continue;
+            f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
+#pragma unroll
+            for (int s = 0; s < G::KS; ++s) {
+                sa = mfma(row_op(rowA[u], 0, s), kreg[s], sa);  // S (queries x this wave's keys)
+                sb = mfma(row_op(rowA[u], 1, s), kreg[s], sb);
+                pa = mfma(row_op(rowB[u], 0, s), vreg[s], pa);  // dP
+                pb = mfma(row_op(rowB[u], 1, s), vreg[s], pb);
+            }
+            float pr0[4], pr1[4], ds0[4], ds1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q0 = qb * BR + 4 * lg + i, q1 = q0 + 16;
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -lse[q0]));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -lse[q1]));
+                pr0[i] = q0 < L ? e0 : 0.0f;
+                pr1[i] = q1 < L ? e1 : 0.0f;
+                ds0[i] = q0 < L ? e0 * (pa[i] - dd[q0]) : 0.0f;
+                ds1[i] = q1 < L ? e1 * (pb[i] - dd[q1]) : 0.0f;
+            }
+            const bf16x8 pp = pack8(pr0, pr1), dsp = pack8(ds0, ds1);
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt) {
+                dvacc[dt] = mfma(tr_op(trB[u], dt), pp, dvacc[dt]);
+                dkacc[dt] = mfma(tr_op(trA[u], dt), dsp, dkacc[dt]);
+            }
+            if (qb == NB - 1) {
+                store_rows(dkacc, scale, kt, addk, dkp, qk_f32 != 0);
+                store_rows(dvacc, 1.0f, kt, nullptr, dvp, false);
+            }
         }
     }
 }
