@@ -363,8 +363,12 @@ def main():
     def glob(s):
         bd.squad_attn_global(s[0], s[1], s[3], grid, window, out=s[3])
 
+    def reversed_order(s):
+        bd.squad_attn_fwd_reversed(s[0], s[1], s[2], grid, window, out=s[3])
+
     local_ms = time_loop(local, args.kernel_iters, sets)
     global_ms = time_loop(glob, args.kernel_iters, sets)
+    reversed_ms = time_loop(reversed_order, max(args.kernel_iters // 5, 5), sets)
     eprint(f"[bench] local pass {local_ms:.4f} ms/launch, global pass {global_ms:.4f} ms/launch, warm fwd {warm_ms:.4f}")
     dom, dom_ms = ("local", local_ms) if local_ms >= global_ms else ("global", global_ms)
     kname = "squad_local_pass" if dom == "local" else "squad_global_pass"
@@ -395,6 +399,7 @@ def main():
         "algorithmic_gbs": bytes_fwd / (ms_per_step * 1e-3) / 1e9,
         "fraction_of_roofline": (bytes_fwd / (ms_per_step * 1e-3) / 1e9) / HBM_PEAK_GBS,
         "kernels_ms": {"squad_local_pass": local_ms, "squad_global_pass": global_ms},
+        "reversed_order_ms": reversed_ms,
         "roofline": {
             "kernel": kname,
             "bound": "hbm",
