@@ -110,3 +110,24 @@ def test_backward_deterministic():
     b = bd.squad_attn_bwd(qd, kd, vd, out, vd, geo[:3], geo[3:])
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+def test_backward_long_windows_sampled_heads():
+    # the 4x 5B block: m = 336 (three groups of query / key tiles per window), N_w = 220
+    import torch
+    w = wl.WORKLOADS["wan5b_4x"]
+    log("case bwd workload=wan5b_4x (generating inputs)")
+    qd, kd, vd = wl.device_inputs(w, seed=0)
+    dod = wl.device_inputs(w, seed=1)[0]
+    grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)
+    out = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    dq, dk, dv = bd.squad_attn_bwd(qd, kd, vd, out, dod, grid, window)
+    torch.cuda.synchronize()
+    table = so.window_slot_table(*grid, *window)
+    for h in (5,):
+        q, k, v = wl.head_slices_f64(w, 0, h)
+        do = to_f64(dod[0, :, h, :])
+        ref = so.squad_backward_head(q, k, v, do, table)
+        check_grads([to_f64(t[0, :, h, :]) for t in (dq, dk, dv)], ref, "bf16", f"wan5b_4x h={h}")
+    del qd, kd, vd, dod, out, dq, dk, dv
+    torch.cuda.empty_cache()
