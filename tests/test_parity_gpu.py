@@ -284,3 +284,27 @@ def test_in_place_long_problems_against_oracle(fn):
         gpu_fn(qd, kd, buf, (T, Hs, Ws), (wt, wh, ww), out=buf)
         torch.cuda.synchronize()
         assert_close(to_f64(buf), ref_fn(q, k, v, (1, heads, T, Hs, Ws, wt, wh, ww, d)), "bf16", f"in place {fn}")
+
+
+def test_graph_capture_replays_match_eager():
+    # the forward enqueues kernels only (no memset, no allocation), so it can
+    # be captured; every replay, with eager work and synchronisation between
+    # replays, must reproduce the eager result exactly
+    import torch
+    T, Hs, Ws, wt, wh, ww = 3, 10, 12, 3, 2, 2
+    q, k, v = wl.random_geometry_inputs(1, 4, T * Hs * Ws, 128, "bf16", seed=29)
+    qd, kd, vd = host_to_device((q, k, v), "bf16")
+    eager = bd.squad_attn_fwd(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww))
+    out = torch.empty_like(qd)
+    bd.squad_attn_fwd(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww), out=out)  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bd.squad_attn_fwd(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww), out=out)
+    for i in range(4):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        bd.squad_attn_local(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww))  # eager work between replays
+        torch.cuda.synchronize()
