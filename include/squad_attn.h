@@ -196,9 +196,10 @@ squad_status_t squad_window_solve(int T, int Hs, int Ws, int* wt, int* wh, int* 
  * receive dL/dq, dL/dk, dL/dv.  All [B, n, heads, d] of one dtype, as for
  * squad_attn_fwd (windows must tile the grid).  workspace: device buffer of at
  * least squad_attn_bwd_workspace_bytes(...) bytes, 16-byte aligned: the
- * recomputed local output Y and dY in the dtype and float32 partial dq, dk
- * (contents on entry ignored; one workspace must not serve calls that may run
- * at the same time).  Three kernels are enqueued on `stream`: the local pass
+ * recomputed local output Y and dY in the dtype, float32 partial dq, dk and,
+ * in bf16, the float32 log-sum-exp of Y's rows (which the local pass's
+ * backward reuses instead of recomputing it) (contents on entry ignored; one
+ * workspace must not serve calls that may run at the same time).  Three kernels are enqueued on `stream`: the local pass
  * (recomputing Y), the global pass's backward, the local pass's backward.
  * P and dS enter the bf16 MFMAs rounded to bf16; sums are float32.
  *

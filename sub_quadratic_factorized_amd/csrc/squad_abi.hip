@@ -212,7 +212,7 @@ PassGeom make_geom(const Problem& pr, bool global) {
 hipError_t run_pass(const Problem& pr, bool global, const void* q, const void* k, const void* vals, void* out,
                     void* ypad, hipStream_t st) {
     const PassGeom g = make_geom(pr, global);
-    if (pr.dtype == SQUAD_BF16) return launch_pass_bf16(g, pr.d, q, k, vals, out, ypad, st);
+    if (pr.dtype == SQUAD_BF16) return launch_pass_bf16(g, pr.d, q, k, vals, out, ypad, nullptr, st);
     return launch_pass_f32(g, pr.d, q, k, vals, out, ypad, st);
 }
 
@@ -227,10 +227,11 @@ hipError_t run_two_passes(const Problem& pr, bool local_first, const void* q, co
 }
 
 // Workspace of the backward: Y (the recomputed local output) and dY in the
-// dtype, then the global pass's float32 contributions to dQ and dK; each
-// region starts on a 256-byte boundary.
+// dtype, then the global pass's float32 contributions to dQ and dK, then the
+// local pass's row log-sum-exp (float32, B*n*heads; bf16 only); each region
+// starts on a 256-byte boundary.
 struct BwdLayout {
-    size_t y, dy, gq, gk, total;
+    size_t y, dy, gq, gk, lse, total;
 };
 
 BwdLayout bwd_layout(const Problem& pr) {
@@ -241,7 +242,8 @@ BwdLayout bwd_layout(const Problem& pr) {
     l.dy = up(e * esize(pr.dtype));
     l.gq = l.dy + up(e * esize(pr.dtype));
     l.gk = l.gq + up(e * 4);
-    l.total = l.gk + up(e * 4);
+    l.lse = l.gk + up(e * 4);
+    l.total = l.lse + (pr.dtype == SQUAD_BF16 ? up(e / pr.d * 4) : 0);
     return l;
 }
 
@@ -289,18 +291,22 @@ hipError_t run_backward(const Problem& pr, const void* q, const void* k, const v
     char* w = static_cast<char*>(ws);
     void *y = w + lay.y, *dy = w + lay.dy;
     float *gq = reinterpret_cast<float*>(w + lay.gq), *gk = reinterpret_cast<float*>(w + lay.gk);
-    // the forward keeps only O: recompute the local output Y
-    hipError_t e = run_pass(pr, false, q, k, v, y, nullptr, st);
-    if (e != hipSuccess) return e;
     const bool bf16 = pr.dtype == SQUAD_BF16;
+    float* lse = bf16 ? reinterpret_cast<float*>(w + lay.lse) : nullptr;
+    // the forward keeps only O: recompute the local output Y (and, in bf16,
+    // its rows' log-sum-exp, which the local pass's backward then reuses)
+    const PassGeom gy = make_geom(pr, false);
+    hipError_t e = bf16 ? launch_pass_bf16(gy, pr.d, q, k, v, y, nullptr, lse, st)
+                        : launch_pass_f32(gy, pr.d, q, k, v, y, nullptr, st);
+    if (e != hipSuccess) return e;
     // global pass (values Y, output O): dQ, dK contributions in float32, dY
     const PassGeom gg = make_geom(pr, true);
-    BwdArgs ag{q, k, y, out, dout, nullptr, nullptr, gq, gk, dy, true};
+    BwdArgs ag{q, k, y, out, dout, nullptr, nullptr, gq, gk, dy, true, nullptr};
     e = bf16 ? launch_bwd_pass_bf16(gg, pr.d, ag, st) : launch_bwd_pass_f32(gg, pr.d, ag, st);
     if (e != hipSuccess) return e;
     // local pass (values V, output Y, upstream dY): adds the global pass's share
     const PassGeom gl = make_geom(pr, false);
-    BwdArgs al{q, k, v, y, dy, gq, gk, dq, dk, dv, !bf16};
+    BwdArgs al{q, k, v, y, dy, gq, gk, dq, dk, dv, !bf16, lse};
     return bf16 ? launch_bwd_pass_bf16(gl, pr.d, al, st) : launch_bwd_pass_f32(gl, pr.d, al, st);
 }
 

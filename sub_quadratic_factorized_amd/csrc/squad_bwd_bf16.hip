@@ -25,7 +25,9 @@
 // dQ^T.  Key sweep (waves own 16-key tiles): a pass over Q and dO
 // accumulating dV^T and dK^T from P and dS recomputed with the stored
 // log-sum-exp and D.  P and dS enter their MFMAs rounded to bf16; all sums
-// are float32.
+// are float32.  When the rows' log-sum-exp is given (HASLSE: the local pass,
+// whose forward the backward has just recomputed), the pass over K for it is
+// skipped.
 #include "squad_internal.h"
 #include "squad_layout.h"
 #include "squad_mfma.h"
@@ -51,12 +53,12 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
     return r;
 }
 
-template <int D>
+template <int D, bool HASLSE>
 __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const uint16_t* __restrict__ op, const uint16_t* __restrict__ dop, const float* __restrict__ addq,
     const float* __restrict__ addk, void* __restrict__ dqp, void* __restrict__ dkp, uint16_t* __restrict__ dvp,
-    int qk_f32, float c_log2, float scale) {
+    const float* __restrict__ lse_in, int qk_f32, float c_log2, float scale) {
     using G = BlockGeo<D>;
     __shared__ __attribute__((aligned(16))) uint16_t rowA[2][BR * G::KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t rowB[2][BR * G::KSTR];
@@ -89,25 +91,29 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     // over K and V (K -> row and transposed layouts, V -> row layout), the
     // dK / dV pass over Q and dO (both -> row and transposed layouts).
     enum { kLse = 0, kDq = 1, kDkv = 2 };
-    const int nsteps_a = ngroups * 2 * NB;  // even: sweep B starts on slot 0
+    // sweep A: per group NB log-sum-exp steps (unless given) and NB dQ steps,
+    // padded to an even count so that sweep B starts on slot 0
+    const int live_a = ngroups * (HASLSE ? 1 : 2) * NB;
+    const int nsteps_a = (live_a + PD - 1) / PD * PD;
     const int nsteps = nsteps_a + ngroups * NB;
     const bool stager = tid < G::NCH;
     const int ch = stager ? tid : G::NCH - 1;
     const int ld_row = ch / G::KC;
     const int ld_col = (ch % G::KC) * 8;
-    int ld_s = 0, ld_blk = 0, ld_kind = kLse;
+    int ld_s = 0, ld_blk = 0, ld_kind = HASLSE ? kDq : kLse;
     u32x4 sx1[PD], sx2[PD];
     auto issue = [&](u32x4& x1, u32x4& x2) {
-        const bool dead = ld_s >= nsteps;
+        const bool pad = ld_s >= live_a && ld_s < nsteps_a;  // the padding step of sweep A
+        const bool dead = pad || ld_s >= nsteps;
         const int64_t a = row(ld_blk * BR + ld_row) + ld_col;
         const uint16_t* p1 = ld_kind == kDkv ? qp : kp;
         const uint16_t* p2 = ld_kind == kDkv ? dop : vp;
         x1 = *reinterpret_cast<const u32x4*>(p1 + (dead ? 0 : a));
         x2 = *reinterpret_cast<const u32x4*>(p2 + (dead || ld_kind == kLse ? 0 : a));
         ++ld_s;
-        if (++ld_blk == NB) {
+        if (!pad && ++ld_blk == NB) {
             ld_blk = 0;
-            ld_kind = ld_s >= nsteps_a ? kDkv : (ld_kind == kLse ? kDq : kLse);
+            ld_kind = ld_s >= live_a ? kDkv : HASLSE ? kDq : (ld_kind == kLse ? kDq : kLse);
         }
     };
     const int t_put = v_chunk_offset<D>(ld_row, ld_col / 8);
@@ -188,13 +194,14 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     for (int s0 = 0; s0 < nsteps_a; s0 += PD) {
 #pragma unroll
         for (int u = 0; u < PD; ++u, ++st) {
-            const int grp = st / (2 * NB), r = st - grp * 2 * NB;
-            const int kind = r < NB ? kLse : kDq, blk = r < NB ? r : r - NB;
+            const int per = HASLSE ? NB : 2 * NB;
+            const int grp = st / per, r = st - grp * per;
+            const int kind = (!HASLSE && r < NB) ? kLse : kDq, blk = (!HASLSE && r >= NB) ? r - NB : r;
             const int qt = grp * NW + wave;
-            const bool active = qt < ntiles;
+            const bool active = st < live_a && qt < ntiles;
             put(sx1[u], sx2[u], u, kind);
             issue(sx1[u], sx2[u]);
-            if (kind == kLse && blk == 0 && active) {
+            if (blk == 0 && active && (HASLSE || kind == kLse)) {
                 load_tile(qp, qt, qreg);
                 load_tile(dop, qt, doreg);
                 const int64_t a = row(qt * 16 + li);
@@ -208,6 +215,15 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
                 Dq = row_sum4(part);
                 m = -INFINITY;
                 l = 0.0f;
+                if (HASLSE) {
+                    lse2 = lse_in[a / D];
+                    if (lg == 0 && qt * 16 + li < L) {
+                        lse[qt * 16 + li] = lse2;
+                        dd[qt * 16 + li] = Dq;
+                    }
+#pragma unroll
+                    for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
+                }
             }
             __syncthreads();
             if (!active) continue;
@@ -325,23 +341,23 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     }
 }
 
-template <int D>
+template <int D, bool HASLSE>
 hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
     const float scale = 1.0f / __builtin_sqrtf((float)D);
     const float c_log2 = 1.4426950408889634f * scale;
-    hipLaunchKernelGGL(squad_bwd_pass_bf16<D>, dim3(g.nprob), dim3(64 * NW), 0, st, g,
+    hipLaunchKernelGGL((squad_bwd_pass_bf16<D, HASLSE>), dim3(g.nprob), dim3(64 * NW), 0, st, g,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.vals), static_cast<const uint16_t*>(a.out),
                        static_cast<const uint16_t*>(a.dout), a.addq, a.addk, a.dq, a.dk,
-                       static_cast<uint16_t*>(a.dvals), a.qk_f32 ? 1 : 0, c_log2, scale);
+                       static_cast<uint16_t*>(a.dvals), a.lse, a.qk_f32 ? 1 : 0, c_log2, scale);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream) {
-    if (d == 128) return launch_d<128>(g, a, stream);
-    return launch_d<64>(g, a, stream);
+    if (a.lse) return d == 128 ? launch_d<128, true>(g, a, stream) : launch_d<64, true>(g, a, stream);
+    return d == 128 ? launch_d<128, false>(g, a, stream) : launch_d<64, false>(g, a, stream);
 }
 
 }  // namespace squad

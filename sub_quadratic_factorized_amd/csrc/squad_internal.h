@@ -163,8 +163,11 @@ __host__ __device__ inline ProblemIndex decode_problem(const PassGeom& g, int p)
 // `ypad` is the side buffer of padded grids (unused when g.pad == 0): the
 // local pass writes the outputs of padded rows there, the global pass reads
 // its values for padded rows from it and stores real rows only.
+// `lse_out` (bf16, unpadded grids; may be null): receives each row's
+// log-sum-exp in log2 units of the scores scaled by log2(e)/sqrt(d),
+// [B, n, heads] float32.
 hipError_t launch_pass_bf16(const PassGeom& g, int d, const void* q, const void* k,
-                            const void* vals, void* out, void* ypad, hipStream_t stream);
+                            const void* vals, void* out, void* ypad, float* lse_out, hipStream_t stream);
 hipError_t launch_pass_f32(const PassGeom& g, int d, const void* q, const void* k,
                            const void* vals, void* out, void* ypad, hipStream_t stream);
 
@@ -179,6 +182,7 @@ struct BwdArgs {
     const float *addq, *addk;
     void *dq, *dk, *dvals;
     bool qk_f32;
+    const float* lse;  // bf16 only, may be null: the rows' log-sum-exp as launch_pass_bf16 writes it
 };
 
 hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream);

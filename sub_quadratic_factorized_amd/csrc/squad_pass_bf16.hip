@@ -60,7 +60,7 @@ using Geo = BlockGeo<D>;
 template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT>
 __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __restrict__ qp,
                                           const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
-                                          uint16_t* yp, float scale_log2) {
+                                          uint16_t* yp, float* lse_out, float scale_log2) {
     using G = Geo<D>;
     static_assert(PD % 2 == 0, "the LDS buffer of a step must be known at compile time");
     constexpr int QROWS = QSTAGE ? (LMAX + BR - 1) / BR * BR : 1;
@@ -349,6 +349,10 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                     }
                     *reinterpret_cast<bf16x8*>(dst + 32 * p) = o;
                 }
+                // optional row log-sum-exp (log2 units, scores scaled by
+                // log2(e)/sqrt(d)) of unpadded grids, [B, n, heads] float32
+                if (!PAD && lse_out && lg == 0)
+                    lse_out[(dst - op) / D] = mrun[t] + __builtin_log2f(osum[t][0]);
             }
         }
     };
@@ -408,15 +412,15 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_local_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
-    uint16_t* yp, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT>(g, qp, kp, vp, op, yp, scale_log2);
+    uint16_t* yp, float* lse_out, float scale_log2) {
+    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_global_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
-    uint16_t* yp, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT>(g, qp, kp, vp, op, yp, scale_log2);
+    uint16_t* yp, float* lse_out, float scale_log2) {
+    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
 int grid_for(const void* kern, int threads, int nprob) {
@@ -460,7 +464,7 @@ int grid_for(const void* kern, int threads, int nprob) {
 // Otherwise 2, 3 or 4 tiles go on each wave.
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT = false>
 hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o, void* y,
-                      hipStream_t st) {
+                      float* lse, hipStream_t st) {
     auto kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>
                         : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>;
     const void* kern = reinterpret_cast<const void*>(kfn);
@@ -473,12 +477,12 @@ hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k
     const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf((float)D);
     hipLaunchKernelGGL(kfn, dim3(grid), dim3(threads), 0, st, g, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
-                       static_cast<uint16_t*>(y), scale_log2);
+                       static_cast<uint16_t*>(y), lse, scale_log2);
     return hipGetLastError();
 }
 
 template <int D, bool PAD>
-hipError_t launch_d(const PassGeom& g0, const void* q, const void* k, const void* v, void* o, void* y,
+hipError_t launch_d(const PassGeom& g0, const void* q, const void* k, const void* v, void* o, void* y, float* lse,
                     hipStream_t st) {
     constexpr int minw = Geo<D>::NCH / 64;
     const int tiles = (g0.L + 15) / 16;
@@ -490,23 +494,23 @@ hipError_t launch_d(const PassGeom& g0, const void* q, const void* k, const void
         g.div_parts = make_fastdiv((uint32_t)g.parts);
     }
     const int waves = g.part_tiles > minw ? g.part_tiles : minw;
-    if (g.parts > 1) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, true>(g, waves, q, k, v, o, y, st);
-    if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true, PAD>(g, waves, q, k, v, o, y, st);
-    if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD>(g, 8, q, k, v, o, y, st);
-    if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD>(g, 8, q, k, v, o, y, st);
-    return launch_one<D, 4, 8, 2, 2, 512, false, PAD>(g, 8, q, k, v, o, y, st);
+    if (g.parts > 1) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, true>(g, waves, q, k, v, o, y, lse, st);
+    if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true, PAD>(g, waves, q, k, v, o, y, lse, st);
+    if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD>(g, 8, q, k, v, o, y, lse, st);
+    if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD>(g, 8, q, k, v, o, y, lse, st);
+    return launch_one<D, 4, 8, 2, 2, 512, false, PAD>(g, 8, q, k, v, o, y, lse, st);
 }
 
 }  // namespace
 
 hipError_t launch_pass_bf16(const PassGeom& g, int d, const void* q, const void* k, const void* vals, void* out,
-                            void* ypad, hipStream_t stream) {
+                            void* ypad, float* lse_out, hipStream_t stream) {
     if (g.pad) {
-        if (d == 128) return launch_d<128, true>(g, q, k, vals, out, ypad, stream);
-        return launch_d<64, true>(g, q, k, vals, out, ypad, stream);
+        if (d == 128) return launch_d<128, true>(g, q, k, vals, out, ypad, nullptr, stream);
+        return launch_d<64, true>(g, q, k, vals, out, ypad, nullptr, stream);
     }
-    if (d == 128) return launch_d<128, false>(g, q, k, vals, out, nullptr, stream);
-    return launch_d<64, false>(g, q, k, vals, out, nullptr, stream);
+    if (d == 128) return launch_d<128, false>(g, q, k, vals, out, nullptr, lse_out, stream);
+    return launch_d<64, false>(g, q, k, vals, out, nullptr, lse_out, stream);
 }
 
 }  // namespace squad

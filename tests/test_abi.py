@@ -275,7 +275,8 @@ def test_window_solver_matches_oracle_rule():
 
 DO, DQ, DK, DV = A + 16 * BYTES, A + 20 * BYTES, A + 24 * BYTES, A + 28 * BYTES
 BWS = A + 32 * BYTES
-BWS_BYTES = 2 * BYTES + 2 * 2 * BYTES  # Y and dY in bf16, float32 dq and dk partials (256-byte rounded: exact here)
+# Y and dY in bf16, float32 dq and dk partials, float32 row log-sum-exp (256-byte rounded: exact here)
+BWS_BYTES = 2 * BYTES + 2 * 2 * BYTES + 18480 * 24 * 4
 
 
 def bcall(fn="check", q=Q, k=K, v=V, out=O, dout=DO, dq=DQ, dk=DK, dv=DV, ws=BWS, ws_bytes=BWS_BYTES,
@@ -291,7 +292,7 @@ def bcall(fn="check", q=Q, k=K, v=V, out=O, dout=DO, dq=DQ, dk=DK, dv=DV, ws=BWS
 
 def test_bwd_workspace_and_helpers():
     assert bd.squad_attn_bwd_workspace_bytes(*GEO.values(), bd.SQUAD_BF16) == BWS_BYTES
-    assert bd.squad_attn_bwd_workspace_bytes(*GEO.values(), bd.SQUAD_F32) == 4 * 2 * BYTES
+    assert bd.squad_attn_bwd_workspace_bytes(*GEO.values(), bd.SQUAD_F32) == 4 * 2 * BYTES  # no log-sum-exp region
     assert bd.squad_attn_bwd_workspace_bytes(*dict(GEO, wh=3).values(), bd.SQUAD_BF16) == -1
     assert bd.squad_attn_bwd_workspace_bytes(*dict(GEO, B=0).values(), bd.SQUAD_BF16) == 0
     assert bd.squad_attn_bwd_flops(*GEO.values()) == 2.5 * 63_128_862_720
