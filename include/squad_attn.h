@@ -44,8 +44,8 @@
  * Errors (checked in this order; the first failing check is returned):
  *   SQUAD_ERR_SHAPE       a negative B or heads; any other dimension < 1;
  *                         T % wt, Hs % wh or Ws % ww != 0; the element count
- *                         B*n*heads*d overflowing 62 bits; B*heads*max(m, N_w)
- *                         not fitting a 31-bit launch grid.
+ *                         B*n*heads*d overflowing 62 bits, or heads*d 31 bits;
+ *                         B*heads*max(m, N_w) not fitting a 31-bit launch grid.
  *   SQUAD_ERR_UNSUPPORTED unknown dtype; d not in {64, 128}; m or N_w above
  *                         squad_attn_max_len(d, dtype).
  *   SQUAD_ERR_NULL        q, k, v or out is NULL.

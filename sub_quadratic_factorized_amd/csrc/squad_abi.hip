@@ -60,9 +60,11 @@ squad_status_t check_shape(int B, int heads, int T, int Hs, int Ws, int wt, int 
         pr->elems = 0;
         return SQUAD_OK;
     }
-    // element count B*n*heads*d must stay below 2^62
+    // element count B*n*heads*d must stay below 2^62, and the token stride
+    // heads*d (an int in the kernels) below 2^31
     const long double el = (long double)B * (long double)n * (long double)heads * (long double)d;
     if (el >= (long double)((int64_t)1 << 62)) return SQUAD_ERR_SHAPE;
+    if ((int64_t)heads * d >= ((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;
     pr->elems = (int64_t)B * n * heads * d;
     // every pass launches at most B*heads*max(m, N_w) problems
     const long double probs = (long double)B * heads * (long double)(m > nw ? m : nw);
@@ -108,6 +110,7 @@ squad_status_t check_shape_padded(int B, int heads, int T, int Hs, int Ws, int w
     }
     const long double el = (long double)B * (long double)np * (long double)heads * (long double)d;
     if (el >= (long double)((int64_t)1 << 62)) return SQUAD_ERR_SHAPE;
+    if ((int64_t)heads * d >= ((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;
     pr->elems = (int64_t)B * n * heads * d;
     const long double probs = (long double)B * heads * (long double)(m > pr->nw ? m : pr->nw);
     if (probs >= (long double)((int64_t)1 << 31)) return SQUAD_ERR_SHAPE;

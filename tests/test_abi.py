@@ -65,6 +65,8 @@ def test_shape_errors(name):
     assert call(name, B=1 << 30, heads=1 << 30, T=1 << 10, Hs=1, Ws=1, wt=1, wh=1, ww=1) == S
     # problem count beyond a 31-bit grid
     assert call(name, B=1 << 20, heads=1 << 10, T=512, Hs=1, Ws=1, wt=1, wh=1, ww=1, d=64) == S
+    # token stride heads * d beyond 31 bits
+    assert call(name, B=1, heads=1 << 24, T=1, Hs=1, Ws=1, wt=1, wh=1, ww=1, d=128) == S
 
 
 @pytest.mark.parametrize("name", bd.COMPUTE_ENTRY_POINTS)
