@@ -7,12 +7,14 @@
 // view is ever materialised in HBM.
 //
 // Workgroup organisation
-//   * Persistent: a workgroup walks problems blockIdx.x, +gridDim.x, ...; one
-//     problem is owned by one workgroup, which reads all of its rows before it
-//     writes any (this is what makes the in-place global pass safe).
-//   * The work of a problem is NB = ceil(L/32) steps.  Step b brings in 32 rows
+//   * Persistent: a workgroup walks work items blockIdx.x, +gridDim.x, ...: a
+//     whole problem, or (long problems of a pass that is not in place) one of
+//     the 2-3 parts of its query rows.  A whole problem is owned by one
+//     workgroup, which reads all of its rows before it writes any (this is
+//     what makes the in-place global pass safe).
+//   * The work of an item is NB = ceil(L/32) steps.  Step b brings in 32 rows
 //     of K and of V (block b of this problem) and 32 rows of Q (block b of the
-//     NEXT problem).  Every thread stages one 16-byte chunk of each in
+//     NEXT item's query rows).  Every thread stages one 16-byte chunk of each in
 //     registers, PD steps ahead of use: ~PD * 3 * 32 * D * 2 bytes per
 //     workgroup are in flight while the MFMAs run.  Loads are unconditional
 //     (clamped addresses), so each stays in flight until its data is stored.
@@ -27,6 +29,8 @@
 //   * Softmax is online across key blocks in the exp2 domain with a lazily
 //     refreshed running maximum (refreshed only when a block's maximum exceeds
 //     it by more than 2^8), so the accumulator rescale is rare and P <= 256.
+//     On request (the backward's recompute of the local output) each row's
+//     log-sum-exp is stored as well.
 #include "squad_internal.h"
 #include "squad_layout.h"
 #include "squad_mfma.h"
