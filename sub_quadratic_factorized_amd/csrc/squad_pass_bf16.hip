@@ -361,14 +361,16 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         }
     };
 
-    // prologue: Q of the first problem straight into the stage, then PD steps in flight
+    // prologue: Q of the first item straight into the stage, then PD steps in
+    // flight.  A wave copies 64 / KC rows per iteration (a 16-byte chunk per
+    // lane), so the start-up waits for few memory round trips.
     if (QSTAGE && nmine > 0) {
         const Prob p0 = problem(0);
-        for (int r = wave; r < QCAP; r += blockDim.x >> 6) {
+        constexpr int RPW = 64 / G::KC;
+        const int c = lane % G::KC;
+        for (int r = wave * RPW + lane / G::KC; r < QCAP; r += (blockDim.x >> 6) * RPW) {
             const int64_t a = src_off(p0, tab[p0.q0 + min(r, p0.qn - 1)]);
-            for (int c = lane; c < G::KC; c += 64)
-                *reinterpret_cast<u32x4*>(&qstage[r * G::KSTR + c * 8]) =
-                    *reinterpret_cast<const u32x4*>(qp + a + c * 8);
+            *reinterpret_cast<u32x4*>(&qstage[r * G::KSTR + c * 8]) = *reinterpret_cast<const u32x4*>(qp + a + c * 8);
         }
     }
 #pragma unroll
