@@ -429,7 +429,11 @@ __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))
     pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
-int grid_for(const void* kern, int threads, int nprob) {
+// Workgroups for a persistent launch over nprob items, a multiple of `mult`
+// (when at least mult fit): as many as fit, less any that would only thin out
+// the last round, so every workgroup walks the same number of items or one
+// fewer.
+int grid_for(const void* kern, int threads, int nprob, int mult) {
     struct Entry {
         const void* k;
         int threads, dev, occ;
@@ -451,8 +455,13 @@ int grid_for(const void* kern, int threads, int nprob) {
         std::lock_guard<std::mutex> lock(mu);
         if (used < 64) cache[used++] = Entry{kern, threads, dev, occ};
     }
-    const long long want = (long long)occ * device_cu_count();
-    return (int)(want < nprob ? want : nprob);
+    long long want = (long long)occ * device_cu_count();
+    if (want >= mult) want -= want % mult;
+    if (want >= nprob) return nprob;
+    const long long rounds = (nprob + want - 1) / want;
+    long long grid = (nprob + rounds - 1) / rounds;
+    if (want >= mult) grid = (grid + mult - 1) / mult * mult;  // still <= want
+    return (int)grid;
 }
 
 // Launch menu.  A problem of length L needs ceil(L/16) query tiles spread over
@@ -478,8 +487,7 @@ hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k
     if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.part_tiles * 16 > LMAX || g.part_tiles > QT * waves ||
         (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0))
         return hipErrorInvalidConfiguration;  // the menu never asks for this
-    int grid = grid_for(kern, threads, g.nitems);
-    if (g.parts > 1 && grid >= 8 * g.parts) grid -= grid % (8 * g.parts);
+    const int grid = grid_for(kern, threads, g.nitems, g.parts > 1 ? 8 * g.parts : 1);
     const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf((float)D);
     hipLaunchKernelGGL(kfn, dim3(grid), dim3(threads), 0, st, g, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
