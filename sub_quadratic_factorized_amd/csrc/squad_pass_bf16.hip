@@ -28,7 +28,8 @@
 //     sum of P is one more MFMA against a tile of ones.
 //   * Softmax is online across key blocks in the exp2 domain with a lazily
 //     refreshed running maximum (refreshed only when a block's maximum exceeds
-//     it by more than 2^8), so the accumulator rescale is rare and P <= 256.
+//     it by more than 2^8), so the accumulator rescale is rare and P <= 256;
+//     the cross-lane reduction of the block maximum runs only then.
 //     On request (the backward's recompute of the local output) each row's
 //     log-sum-exp is stored as well.
 #include "squad_internal.h"
@@ -60,8 +61,12 @@ using Geo = BlockGeo<D>;
 // named by packed padded coordinates; q, k and the local pass's values read
 // through mirror images; padded rows of Y in the side buffer yp).  SPLIT:
 // items are parts of problems (PassGeom::parts > 1); otherwise items are
-// whole problems and the part logic compiles away.
-template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT>
+// whole problems and the part logic compiles away.  FAST (unpadded grids whose
+// batch elements span less than 4 GiB per tensor): loads and stores go
+// through buffer descriptors based at a problem's base row, so a chunk's
+// address is a single 32-bit offset, and loads of dead steps return zeros
+// without a memory access.
+template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT, bool FAST>
 __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __restrict__ qp,
                                           const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
                                           uint16_t* yp, float* lse_out, float scale_log2) {
@@ -71,7 +76,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][BR * G::KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][BR * G::VSTR];
     __shared__ __attribute__((aligned(16))) uint16_t qstage[QROWS * G::KSTR];
-    __shared__ int tab[kMaxLen];
+    __shared__ uint32_t tab[kMaxLen];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -93,9 +98,15 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     const int ld_col = (ch % G::KC) * 8;
 
     // row r of any problem of this pass sits at a fixed token offset from the
-    // problem's base token (padded grids: at fixed packed coordinates)
-    for (int r = tid; r < L; r += blockDim.x)
-        tab[r] = PAD ? (GP ? win_coords(g, r) : slot_coords(g, r)) : (GP ? win_origin(g, r) : slot_offset(g, r));
+    // problem's base token (padded grids: at fixed packed coordinates; FAST:
+    // the offset in bytes, and the table filled up to whole blocks with the
+    // last row, so the loader needs no clamp)
+    static_assert(!(FAST && PAD), "FAST is for unpadded grids");
+    for (int r = tid; r < (FAST ? NB * BR : L); r += blockDim.x) {
+        const int rr = FAST ? min(r, L - 1) : r;
+        const int tv = PAD ? (GP ? win_coords(g, rr) : slot_coords(g, rr)) : (GP ? win_origin(g, rr) : slot_offset(g, rr));
+        tab[r] = FAST ? (uint32_t)tv * (uint32_t)(row_stride * 2) : (uint32_t)tv;
+    }
     __syncthreads();
 
     // A work item: unpadded, the offset of its problem's base token row (row
@@ -125,9 +136,20 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0, q0, qn};
     };
     // offset, in q, k and the local pass's values, of the row with table entry tv
-    auto src_off = [&](const Prob& pr, int tv) -> int64_t {
-        if (PAD) return pr.off + (int64_t)mirrored_token(g, pr.base + tv) * row_stride;
+    auto src_off = [&](const Prob& pr, uint32_t tv) -> int64_t {
+        if (PAD) return pr.off + (int64_t)mirrored_token(g, pr.base + (int)tv) * row_stride;
+        if (FAST) return pr.off + (int64_t)(tv >> 1);
         return pr.off + (int64_t)tv * row_stride;
+    };
+    // FAST: a buffer descriptor based at a problem's base row covering the
+    // rest of the tensor (none when the problem is dead)
+    const int64_t tensor_elems = (int64_t)(g.nprob / g.P) * g.n * D;
+    auto rsrc = [&](const void* base, const Prob& pr, bool live) {
+        const int64_t left = (tensor_elems - pr.off) * 2;
+        const uint32_t nrec = !live ? 0u : left >= (int64_t)0xffffffffu ? 0xffffffffu : (uint32_t)left;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(static_cast<const uint16_t*>(base)) + (live ? pr.off : 0), 0, (int)nrec,
+            0x00020000);
     };
 
     // ---- loader -------------------------------------------------------------
@@ -145,22 +167,64 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0, 0, 1};
     Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0, 0, 1};
 
+    // FAST: descriptors of the loader's problems, and this thread's row
+    // offsets for the next call (read one call ahead)
+    const uint32_t col_bytes = (uint32_t)ld_col * 2u;
+    __amdgpu_buffer_rsrc_t rk, rv, rq, rdead;
+    uint32_t nk_off = 0, nq_off = 0;
+    if constexpr (FAST) {
+        rk = rsrc(kp, ld_p, !ld_dead);
+        rv = rsrc(vp, ld_p, !ld_dead);
+        rq = rsrc(qp, ld_q, !q_dead);
+        rdead = rsrc(qp, ld_q, false);
+        nk_off = tab[ld_row];
+        if (SPLIT) nq_off = tab[ld_q.q0 + min(ld_row, ld_q.qn - 1)];
+    }
+    auto issue_fast = [&](u32x4& dk, u32x4& dv, u32x4& dq) {
+        const uint32_t o = nk_off + col_bytes;
+        dk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+        dv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+        if (QSTAGE) {
+            if (SPLIT)
+                dq = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   ld_b * BR >= ld_q.qn ? rdead : rq, nq_off + col_bytes, 0, 0));
+            else
+                dq = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0));
+        }
+        if (++ld_b == NB) {
+            ld_b = 0;
+            ++ld_it;
+            ld_dead = ld_it >= nmine;
+            q_dead = ld_it + 1 >= nmine;
+            ld_p = ld_q;
+            if (!q_dead) ld_q = problem(ld_it + 1);
+            rk = rsrc(kp, ld_p, !ld_dead);
+            rv = rsrc(vp, ld_p, !ld_dead);
+            rq = rsrc(qp, ld_q, !q_dead);
+        }
+        nk_off = tab[ld_b * BR + ld_row];
+        if (SPLIT) nq_off = tab[ld_q.q0 + min(ld_b * BR + ld_row, ld_q.qn - 1)];
+    };
     auto issue = [&](u32x4& dk, u32x4& dv, u32x4& dq) {
-        const int tv = tab[min(ld_b * BR + ld_row, L - 1)];
+        if constexpr (FAST) {
+            issue_fast(dk, dv, dq);
+            return;
+        }
+        const uint32_t tv = tab[min(ld_b * BR + ld_row, L - 1)];
         const int64_t a = src_off(ld_p, tv) + ld_col;
         // the global pass's values are the local outputs: on a padded grid a
         // padded row's come from the side buffer
         const uint16_t* vb = vp;
         int64_t av = a;
-        if (PAD && GP && !is_real(g, ld_p.base + tv)) {
+        if (PAD && GP && !is_real(g, ld_p.base + (int)tv)) {
             vb = yp;
-            av = ld_p.yoff + (int64_t)pad_index(g, ld_p.base + tv) * row_stride + ld_col;
+            av = ld_p.yoff + (int64_t)pad_index(g, ld_p.base + (int)tv) * row_stride + ld_col;
         }
         dk = *reinterpret_cast<const u32x4*>(kp + (ld_dead ? 0 : a));
         dv = *reinterpret_cast<const u32x4*>(vb + (ld_dead ? 0 : av));
         if (QSTAGE) {
             // row of the next item's query rows (unsplit: the key / value row)
-            const int tq = SPLIT ? tab[ld_q.q0 + min(ld_b * BR + ld_row, ld_q.qn - 1)] : tv;
+            const uint32_t tq = SPLIT ? tab[ld_q.q0 + min(ld_b * BR + ld_row, ld_q.qn - 1)] : tv;
             const bool qd = q_dead || (SPLIT && ld_b * BR >= ld_q.qn);
             dq = *reinterpret_cast<const u32x4*>(qp + (qd ? 0 : src_off(ld_q, tq) + ld_col));
         }
@@ -174,15 +238,17 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         }
     };
 
-    // swizzled position of this thread's V chunk (16-byte aligned) and whether
-    // its halves are stored swapped (done in registers)
+    // swizzled position of this thread's V chunk (16-byte aligned); its two
+    // 8-byte halves go to fixed addresses (swapped on alternate row groups)
     const int v_put = v_chunk_offset<D>(ld_row, ld_col / 8);
     const bool v_swap = v_halves_swapped<D>(ld_row);
+    const int v_lo = v_put + (v_swap ? 4 : 0), v_hi = v_put + (v_swap ? 0 : 4);
 
     auto put = [&](const u32x4& dk, const u32x4& dv, const u32x4& dq, int buf, int blk) {
         if (stager) {
             *reinterpret_cast<u32x4*>(&kbuf[buf][ld_row * G::KSTR + ld_col]) = dk;
-            *reinterpret_cast<u32x4*>(&vbuf[buf][v_put]) = v_swap ? u32x4{dv.z, dv.w, dv.x, dv.y} : dv;
+            *reinterpret_cast<u32x2*>(&vbuf[buf][v_lo]) = u32x2{dv.x, dv.y};
+            *reinterpret_cast<u32x2*>(&vbuf[buf][v_hi]) = u32x2{dv.z, dv.w};
             if (QSTAGE && (!SPLIT || blk * BR < QCAP))
                 *reinterpret_cast<u32x4*>(&qstage[(blk * BR + ld_row) * G::KSTR + ld_col]) = dq;
         }
@@ -195,6 +261,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     bf16x8 pk[QT];
     float mrun[QT];
     Prob cur_p{0, 0, 0, 0, 1};
+    __amdgpu_buffer_rsrc_t ro;
+    if constexpr (FAST) ro = rsrc(op, cur_p, false);
     int c_it = 0;
     // waves past the item's last query tile only stage data; a wave's partial
     // tiles compute on clamped rows and are never stored (unsplit: the same
@@ -224,6 +292,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 
     auto start_problem = [&]() {
         cur_p = problem(c_it);
+        if constexpr (FAST) ro = rsrc(op, cur_p, true);
         if (SPLIT) computes = wave * QT * 16 < cur_p.qn;
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
@@ -271,9 +340,11 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                 }
                 float mx = fmaxf(fmaxf(fmaxf(s0[t][0], s0[t][1]), fmaxf(s0[t][2], s0[t][3])),
                                  fmaxf(fmaxf(s1[t][0], s1[t][1]), fmaxf(s1[t][2], s1[t][3])));
-                mx = row_max4(mx) * scale_log2;
-                const float mnew = fmaxf(mrun[t], mx);
-                if (__builtin_amdgcn_ballot_w64(mnew > mrun[t] + kRescaleHeadroom) != 0) {
+                // a lane's own keys decide whether the row needs a new running
+                // maximum (exactly when the row's keys do); only then is the
+                // maximum reduced across the row's four lanes
+                if (__builtin_amdgcn_ballot_w64(mx * scale_log2 > mrun[t] + kRescaleHeadroom) != 0) {
+                    const float mnew = fmaxf(mrun[t], row_max4(mx) * scale_log2);
                     const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
                     osum[t] *= alpha;
 #pragma unroll
@@ -330,16 +401,37 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             // padded grids: real rows to out, padded rows of the local pass to
             // the side buffer, padded rows of the global pass nowhere (cropped)
             bool keep = row < cur_p.qn;
+            if constexpr (FAST) {
+                if (keep) {
+                    const uint32_t tv = tab[cur_p.q0 + row];
+#pragma unroll
+                    for (int p = 0; p < D / 32; ++p) {
+                        bf16x8 o;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            o[i] = static_cast<__bf16>(oacc[t][2 * p][i] * inv);
+                            o[4 + i] = static_cast<__bf16>(oacc[t][2 * p + 1][i] * inv);
+                        }
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro,
+                                                               tv + 16u * lg + 64u * p, 0, 0);
+                    }
+                    // optional row log-sum-exp (log2 units, scores scaled by
+                    // log2(e)/sqrt(d)), [B, n, heads] float32
+                    if (lse_out && lg == 0)
+                        lse_out[(cur_p.off + (int64_t)(tv >> 1)) / D] = mrun[t] + __builtin_log2f(osum[t][0]);
+                }
+                continue;
+            }
             uint16_t* dst = op;
             if (keep) {
-                const int tv = tab[cur_p.q0 + row];
+                const uint32_t tv = tab[cur_p.q0 + row];
                 if (!PAD) {
                     dst = op + cur_p.off + (int64_t)tv * row_stride + 8 * lg;
-                } else if (is_real(g, cur_p.base + tv)) {
+                } else if (is_real(g, cur_p.base + (int)tv)) {
                     dst = op + src_off(cur_p, tv) + 8 * lg;
                 } else {
                     keep = !GP;
-                    dst = yp + cur_p.yoff + (int64_t)pad_index(g, cur_p.base + tv) * row_stride + 8 * lg;
+                    dst = yp + cur_p.yoff + (int64_t)pad_index(g, cur_p.base + (int)tv) * row_stride + 8 * lg;
                 }
             }
             if (keep) {
@@ -415,24 +507,32 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 }
 
 // The two passes as distinct kernels (so profiles tell them apart).
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT, bool FAST>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_local_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float* lse_out, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT, FAST>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_global_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float* lse_out, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT, false>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
 // Workgroups for a persistent launch over nprob items, a multiple of `mult`
 // (when at least mult fit): as many as fit, less any that would only thin out
 // the last round, so every workgroup walks the same number of items or one
 // fewer.
+// The FAST loader's 32-bit byte offsets: a row's offset from its problem's base
+// row, plus a chunk's column, stays below 2^32 when a batch element of a
+// tensor spans less than 4 GiB (minus a row).
+template <int D>
+bool fast_ok(const PassGeom& g) {
+    return !g.pad && (int64_t)g.n * g.heads * D * 2 + (int64_t)g.heads * D * 2 <= (int64_t)0xffffffffu;
+}
+
 int grid_for(const void* kern, int threads, int nprob, int mult) {
     struct Entry {
         const void* k;
@@ -476,16 +576,23 @@ int grid_for(const void* kern, int threads, int nprob, int mult) {
 // problem are 8 items apart and the grid is a multiple of 8 * parts, so they
 // run in the same round on workgroups 8 apart, which round-robin dispatch puts
 // on the same XCD, and their repeated key / value reads are served by its L2.
-// Otherwise 2, 3 or 4 tiles go on each wave.
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT = false>
+// Otherwise 2, 3 or 4 tiles go on each wave.  The unpadded local pass takes
+// the FAST loader when a batch element of a tensor spans less than 4 GiB.
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool FAST, bool SPLIT = false>
 hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o, void* y,
                       float* lse, hipStream_t st) {
-    auto kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>
-                        : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>;
+    using KernelFn = void (*)(PassGeom, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, uint16_t*,
+                              float*, float);
+    KernelFn kfn;
+    if constexpr (FAST)
+        kfn = &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, true>;
+    else
+        kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>
+                       : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, false>;
     const void* kern = reinterpret_cast<const void*>(kfn);
     const int threads = 64 * waves;
     if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.part_tiles * 16 > LMAX || g.part_tiles > QT * waves ||
-        (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0))
+        (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0) || (FAST && (g.global || !fast_ok<D>(g))))
         return hipErrorInvalidConfiguration;  // the menu never asks for this
     const int grid = grid_for(kern, threads, g.nitems, g.parts > 1 ? 8 * g.parts : 1);
     const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf((float)D);
@@ -495,9 +602,9 @@ hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k
     return hipGetLastError();
 }
 
-template <int D, bool PAD>
-hipError_t launch_d(const PassGeom& g0, const void* q, const void* k, const void* v, void* o, void* y, float* lse,
-                    hipStream_t st) {
+template <int D, bool PAD, bool FAST>
+hipError_t launch_menu(const PassGeom& g0, const void* q, const void* k, const void* v, void* o, void* y, float* lse,
+                       hipStream_t st) {
     constexpr int minw = Geo<D>::NCH / 64;
     const int tiles = (g0.L + 15) / 16;
     PassGeom g = g0;
@@ -508,11 +615,19 @@ hipError_t launch_d(const PassGeom& g0, const void* q, const void* k, const void
         g.div_parts = make_fastdiv((uint32_t)g.parts);
     }
     const int waves = g.part_tiles > minw ? g.part_tiles : minw;
-    if (g.parts > 1) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, true>(g, waves, q, k, v, o, y, lse, st);
-    if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true, PAD>(g, waves, q, k, v, o, y, lse, st);
-    if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD>(g, 8, q, k, v, o, y, lse, st);
-    if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD>(g, 8, q, k, v, o, y, lse, st);
-    return launch_one<D, 4, 8, 2, 2, 512, false, PAD>(g, 8, q, k, v, o, y, lse, st);
+    if (g.parts > 1) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, FAST, true>(g, waves, q, k, v, o, y, lse, st);
+    if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, FAST>(g, waves, q, k, v, o, y, lse, st);
+    if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
+    if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
+    return launch_one<D, 4, 8, 2, 2, 512, false, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
+}
+
+template <int D, bool PAD>
+hipError_t launch_d(const PassGeom& g, const void* q, const void* k, const void* v, void* o, void* y, float* lse,
+                    hipStream_t st) {
+    if constexpr (!PAD)
+        if (!g.global && fast_ok<D>(g)) return launch_menu<D, false, true>(g, q, k, v, o, y, lse, st);
+    return launch_menu<D, PAD, false>(g, q, k, v, o, y, lse, st);
 }
 
 }  // namespace

@@ -286,6 +286,31 @@ def test_in_place_long_problems_against_oracle(fn):
         assert_close(to_f64(buf), ref_fn(q, k, v, (1, heads, T, Hs, Ws, wt, wh, ww, d)), "bf16", f"in place {fn}")
 
 
+@pytest.mark.parametrize("op", ["fwd", "local", "reversed"])
+def test_tensors_beyond_4gib_per_batch_element(op):
+    # 48 tokens x 360,000 heads x d = 128 in bf16 spans 4.4 GB per tensor: the
+    # local pass then takes its 64-bit loader (the 32-bit one needs a batch
+    # element to span less than 4 GiB) and every pass addresses rows beyond
+    # 2^32 bytes; sampled heads, first and last included, against the oracle
+    import torch
+    T, Hs, Ws, wt, wh, ww = 3, 4, 4, 3, 2, 2
+    heads, d = 360_000, 128
+    n = T * Hs * Ws
+    log(f"case {op} beyond 4 GiB: grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} heads={heads} d={d}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(31)
+    q, k, v = (torch.randn(1, n, heads, d, device="cuda", dtype=torch.bfloat16, generator=gen) for _ in range(3))
+    gpu_fn, ref_fn = OPS[op]
+    out = gpu_fn(q, k, v, (T, Hs, Ws), (wt, wh, ww))
+    torch.cuda.synchronize()
+    for h in (0, 1, 180_001, heads - 1):
+        qs, ks, vs = (to_f64(x[:, :, h:h + 1, :].contiguous()) for x in (q, k, v))
+        ref = ref_fn(qs, ks, vs, (1, 1, T, Hs, Ws, wt, wh, ww, d))
+        assert_close(to_f64(out[:, :, h:h + 1, :].contiguous()), ref, "bf16", f"{op} beyond 4 GiB, head {h}")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+
 def test_graph_capture_replays_match_eager():
     # the forward enqueues kernels only (no memset, no allocation), so it can
     # be captured; every replay, with eager work and synchronisation between
