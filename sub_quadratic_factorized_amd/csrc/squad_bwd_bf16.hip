@@ -37,7 +37,7 @@ namespace {
 
 constexpr int BR = kBlockRows;
 constexpr int NW = 8;  // waves per workgroup
-constexpr int PD = 2;  // steps in flight
+constexpr int PD = 4;  // steps in flight (even: LDS buffers alternate by step parity)
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     // dK / dV pass over Q and dO (both -> row and transposed layouts).
     enum { kLse = 0, kDq = 1, kDkv = 2 };
     // sweep A: per group NB log-sum-exp steps (unless given) and NB dQ steps,
-    // padded to an even count so that sweep B starts on slot 0
+    // padded to a multiple of PD so that sweep B starts on slot 0
     const int live_a = ngroups * (HASLSE ? 1 : 2) * NB;
     const int nsteps_a = (live_a + PD - 1) / PD * PD;
     const int nsteps = nsteps_a + ngroups * NB;
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
             const int kind = (!HASLSE && r < NB) ? kLse : kDq, blk = (!HASLSE && r >= NB) ? r - NB : r;
             const int qt = grp * NW + wave;
             const bool active = st < live_a && qt < ntiles;
-            put(sx1[u], sx2[u], u, kind);
+            put(sx1[u], sx2[u], u & 1, kind);
             issue(sx1[u], sx2[u]);
             if (blk == 0 && active && (HASLSE || kind == kLse)) {
                 load_tile(qp, qt, qreg);
@@ -232,8 +232,8 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
                 f32x4 sa = zero, sb = zero;
 #pragma unroll
                 for (int s = 0; s < G::KS; ++s) {
-                    sa = mfma(row_op(rowA[u], 0, s), qreg[s], sa);
-                    sb = mfma(row_op(rowA[u], 1, s), qreg[s], sb);
+                    sa = mfma(row_op(rowA[u & 1], 0, s), qreg[s], sa);
+                    sb = mfma(row_op(rowA[u & 1], 1, s), qreg[s], sb);
                 }
                 float mx = -INFINITY;
 #pragma unroll
@@ -264,10 +264,10 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
                 f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
 #pragma unroll
                 for (int s = 0; s < G::KS; ++s) {
-                    sa = mfma(row_op(rowA[u], 0, s), qreg[s], sa);
-                    sb = mfma(row_op(rowA[u], 1, s), qreg[s], sb);
-                    pa = mfma(row_op(rowB[u], 0, s), doreg[s], pa);  // dP^T
-                    pb = mfma(row_op(rowB[u], 1, s), doreg[s], pb);
+                    sa = mfma(row_op(rowA[u & 1], 0, s), qreg[s], sa);
+                    sb = mfma(row_op(rowA[u & 1], 1, s), qreg[s], sb);
+                    pa = mfma(row_op(rowB[u & 1], 0, s), doreg[s], pa);  // dP^T
+                    pb = mfma(row_op(rowB[u & 1], 1, s), doreg[s], pb);
                 }
                 float ds0[4], ds1[4];
 #pragma unroll
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
                 }
                 const bf16x8 dsk = pack8(ds0, ds1);
 #pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = mfma(tr_op(trA[u], dt), dsk, dqacc[dt]);
+                for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = mfma(tr_op(trA[u & 1], dt), dsk, dqacc[dt]);
                 if (blk == NB - 1) store_rows(dqacc, scale, qt, addq, dqp, qk_f32 != 0);
             }
         }
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
             const int grp = st / NB, qb = st - grp * NB;
             const int kt = grp * NW + wave;
             const bool active = live && kt < ntiles;
-            put(sx1[u], sx2[u], u, kDkv);
+            put(sx1[u], sx2[u], u & 1, kDkv);
             issue(sx1[u], sx2[u]);
             if (active && qb == 0) {
                 load_tile(kp, kt, kreg);
@@ -311,10 +311,10 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
             f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
 #pragma unroll
             for (int s = 0; s < G::KS; ++s) {
-                sa = mfma(row_op(rowA[u], 0, s), kreg[s], sa);  // S (queries x this wave's keys)
-                sb = mfma(row_op(rowA[u], 1, s), kreg[s], sb);
-                pa = mfma(row_op(rowB[u], 0, s), vreg[s], pa);  // dP
-                pb = mfma(row_op(rowB[u], 1, s), vreg[s], pb);
+                sa = mfma(row_op(rowA[u & 1], 0, s), kreg[s], sa);  // S (queries x this wave's keys)
+                sb = mfma(row_op(rowA[u & 1], 1, s), kreg[s], sb);
+                pa = mfma(row_op(rowB[u & 1], 0, s), vreg[s], pa);  // dP
+                pb = mfma(row_op(rowB[u & 1], 1, s), vreg[s], pb);
             }
             float pr0[4], pr1[4], ds0[4], ds1[4];
 #pragma unroll
@@ -330,8 +330,8 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
             const bf16x8 pp = pack8(pr0, pr1), dsp = pack8(ds0, ds1);
 #pragma unroll
             for (int dt = 0; dt < G::DT; ++dt) {
-                dvacc[dt] = mfma(tr_op(trB[u], dt), pp, dvacc[dt]);
-                dkacc[dt] = mfma(tr_op(trA[u], dt), dsp, dkacc[dt]);
+                dvacc[dt] = mfma(tr_op(trB[u & 1], dt), pp, dvacc[dt]);
+                dkacc[dt] = mfma(tr_op(trA[u & 1], dt), dsp, dkacc[dt]);
             }
             if (qb == NB - 1) {
                 store_rows(dkacc, scale, kt, addk, dkp, qk_f32 != 0);
