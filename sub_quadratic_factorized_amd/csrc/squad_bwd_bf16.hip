@@ -6,7 +6,7 @@
 //     D = rowsum(dO * O),  dP = dO V^T,  dS = P * (dP - D),
 //     dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
 //
-// One workgroup of 8 waves per problem; rows stream through LDS in blocks of
+// One workgroup of 8 or 12 waves per problem; rows stream through LDS in blocks of
 // 32 (clamped past the end, masked) along one sequence of steps: per group of
 // query tiles, NB steps over K then NB over K and V; per group of key tiles,
 // NB steps over Q and dO.  Every thread stages one 16-byte chunk of each of
@@ -36,8 +36,6 @@ namespace squad {
 namespace {
 
 constexpr int BR = kBlockRows;
-constexpr int NW = 8;  // waves per workgroup
-constexpr int PD = 4;  // steps in flight (even: LDS buffers alternate by step parity)
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -53,8 +51,11 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
     return r;
 }
 
-template <int D, bool HASLSE>
-__global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
+// NW: waves per workgroup (8: 256 VGPRs; 12: 168, so that problems of 9-12
+// query tiles take one group per sweep instead of two); PD: steps in flight
+// (even: the LDS buffers alternate by step parity).
+template <int D, bool HASLSE, int NW, int PD>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : 2))) void squad_bwd_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
     const uint16_t* __restrict__ op, const uint16_t* __restrict__ dop, const float* __restrict__ addq,
     const float* __restrict__ addk, void* __restrict__ dqp, void* __restrict__ dkp, uint16_t* __restrict__ dvp,
@@ -341,16 +342,26 @@ __global__ __launch_bounds__(64 * NW) void squad_bwd_pass_bf16(
     }
 }
 
-template <int D, bool HASLSE>
-hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
+template <int D, bool HASLSE, int NW, int PD>
+hipError_t launch_nw(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
     const float scale = 1.0f / __builtin_sqrtf((float)D);
     const float c_log2 = 1.4426950408889634f * scale;
-    hipLaunchKernelGGL((squad_bwd_pass_bf16<D, HASLSE>), dim3(g.nprob), dim3(64 * NW), 0, st, g,
+    hipLaunchKernelGGL((squad_bwd_pass_bf16<D, HASLSE, NW, PD>), dim3(g.nprob), dim3(64 * NW), 0, st, g,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.vals), static_cast<const uint16_t*>(a.out),
                        static_cast<const uint16_t*>(a.dout), a.addq, a.addk, a.dq, a.dk,
                        static_cast<uint16_t*>(a.dvals), a.lse, a.qk_f32 ? 1 : 0, c_log2, scale);
     return hipGetLastError();
+}
+
+// 12 waves when they save a group of query / key tiles over 8 waves (at the
+// cost of a few spilled registers and two steps in flight), else 8 waves with
+// four steps in flight
+template <int D, bool HASLSE>
+hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
+    const int tiles = (g.L + 15) / 16;
+    if ((tiles + 11) / 12 < (tiles + 7) / 8) return launch_nw<D, HASLSE, 12, 2>(g, a, st);
+    return launch_nw<D, HASLSE, 8, 4>(g, a, st);
 }
 
 }  // namespace
