@@ -17,7 +17,9 @@
 //     NEXT item's query rows).  Every thread stages one 16-byte chunk of each in
 //     registers, PD steps ahead of use: ~PD * 3 * 32 * D * 2 bytes per
 //     workgroup are in flight while the MFMAs run.  Loads are unconditional
-//     (clamped addresses), so each stays in flight until its data is stored.
+//     (rows past the end clamped to the last row; steps past the last item
+//     read one fixed chunk, or, through buffer descriptors, nothing), so each
+//     stays in flight until its data is stored.
 //   * K and V blocks go to double-buffered LDS slots (one barrier per step);
 //     Q blocks go to an LDS Q stage from which each wave copies its 16-row
 //     query tiles into registers at the first step of the problem.
@@ -104,13 +106,15 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     static_assert(!(FAST && PAD), "FAST is for unpadded grids");
     for (int r = tid; r < (FAST ? NB * BR : L); r += blockDim.x) {
         const int rr = FAST ? min(r, L - 1) : r;
-        const int tv = PAD ? (GP ? win_coords(g, rr) : slot_coords(g, rr)) : (GP ? win_origin(g, rr) : slot_offset(g, rr));
+        const int tv = PAD ? (GP ? win_coords(g, rr) : slot_coords(g, rr))
+                           : (GP ? win_origin(g, rr) : slot_offset(g, rr));
         tab[r] = FAST ? (uint32_t)tv * (uint32_t)(row_stride * 2) : (uint32_t)tv;
     }
     __syncthreads();
 
     // A work item: unpadded, the offset of its problem's base token row (row
-    // r adds tab[r] * row_stride); padded, the (b, h) offsets into the tensors
+    // r adds tab[r] * row_stride elements, FAST tab[r] bytes); padded, the
+    // (b, h) offsets into the tensors
     // and into the side buffer, and the packed base coordinates; and its query
     // rows q0 .. q0 + qn - 1 of the problem.
     struct Prob {
