@@ -6,28 +6,29 @@
 //     D = rowsum(dO * O),  dP = dO V^T,  dS = P * (dP - D),
 //     dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
 //
-// One workgroup of 8 or 12 waves per problem; rows stream through LDS in blocks of
-// 32 (clamped past the end, masked) along one sequence of steps: per group of
-// query tiles, NB steps over K then NB over K and V; per group of key tiles,
-// NB steps over Q and dO.  Every thread stages one 16-byte chunk of each of
-// the step's (up to) two tensors in registers PD steps ahead of use, with
-// unconditional loads, into double-buffered LDS, one barrier per step.  Two
-// kinds of MFMA product occur, both on v_mfma_f32_16x16x32_bf16 with the
-// operand layouts of the forward kernel:
+// One workgroup of 8 or 12 waves per problem; rows stream through LDS in
+// blocks of 32 (clamped past the end, masked) along one sequence of steps: per
+// group of query tiles, NB steps over K and V; per group of key tiles, NB steps
+// over Q and dO.  Every thread stages one 16-byte chunk of each of the step's
+// two tensors in registers PD steps ahead of use, with unconditional loads,
+// into double-buffered LDS, one barrier per step.  Two kinds of MFMA product
+// occur, both on v_mfma_f32_16x16x32_bf16 with the operand layouts of the
+// forward kernel:
 //   * over d (S, dP): both operands are token rows, read as 16-byte row
 //     chunks (the K/Q row layout in LDS, or registers loaded from memory);
 //   * over tokens (dQ^T = K^T dS^T, dV^T = dO^T P, dK^T = Q^T dS): the A
 //     operand is a block read transposed (the V layout and ds_read_b64_tr_b16
 //     fetch of the forward kernel), the B operand is a 16x16 result tile pair
 //     of the first kind packed to bf16 (its rows are the contracted tokens).
-// Query sweep (waves own 16-query tiles): a pass over K for the row maximum
-// and log-sum-exp, D from dO and O, then a pass over K and V accumulating
-// dQ^T.  Key sweep (waves own 16-key tiles): a pass over Q and dO
-// accumulating dV^T and dK^T from P and dS recomputed with the stored
-// log-sum-exp and D.  P and dS enter their MFMAs rounded to bf16; all sums
-// are float32.  When the rows' log-sum-exp is given (HASLSE: the local pass,
-// whose forward the backward has just recomputed), the pass over K for it is
-// skipped.
+// Query sweep (waves own 16-query tiles): D from dO and O, then one pass over
+// K and V accumulating dQ^T; when the rows' log-sum-exp is given (HASLSE: the
+// local pass, whose forward the backward has just recomputed) P is formed from
+// it, otherwise dQ^T accumulates unnormalised probabilities under a running
+// maximum and is divided by the row sum at the end of the pass, which also
+// yields the log-sum-exp.  Key sweep (waves own 16-key tiles): a pass over Q
+// and dO accumulating dV^T and dK^T from P and dS recomputed with the stored
+// log-sum-exp and D.  P and dS enter their MFMAs rounded to bf16; all sums are
+// float32.
 #include "squad_internal.h"
 #include "squad_layout.h"
 #include "squad_mfma.h"
@@ -88,20 +89,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
     auto row = [&](int r) -> int64_t { return bh + (int64_t)(base + tab[min(r, L - 1)]) * row_stride; };
 
     // ---- loader ---------------------------------------------------------------
-    // Step kinds: the log-sum-exp pass over K (K -> row layout), the dQ pass
-    // over K and V (K -> row and transposed layouts, V -> row layout), the
-    // dK / dV pass over Q and dO (both -> row and transposed layouts).
-    enum { kLse = 0, kDq = 1, kDkv = 2 };
-    // sweep A: per group NB log-sum-exp steps (unless given) and NB dQ steps,
-    // padded to a multiple of PD so that sweep B starts on slot 0
-    const int live_a = ngroups * (HASLSE ? 1 : 2) * NB;
+    // Step kinds: the dQ pass over K and V (K -> row and transposed layouts,
+    // V -> row layout), the dK / dV pass over Q and dO (both -> row and
+    // transposed layouts).
+    enum { kDq = 1, kDkv = 2 };
+    // sweep A: per group NB dQ steps, padded to a multiple of PD so that
+    // sweep B starts on slot 0
+    const int live_a = ngroups * NB;
     const int nsteps_a = (live_a + PD - 1) / PD * PD;
     const int nsteps = nsteps_a + ngroups * NB;
     const bool stager = tid < G::NCH;
     const int ch = stager ? tid : G::NCH - 1;
     const int ld_row = ch / G::KC;
     const int ld_col = (ch % G::KC) * 8;
-    int ld_s = 0, ld_blk = 0, ld_kind = HASLSE ? kDq : kLse;
+    int ld_s = 0, ld_blk = 0, ld_kind = kDq;
     u32x4 sx1[PD], sx2[PD];
     auto issue = [&](u32x4& x1, u32x4& x2) {
         const bool pad = ld_s >= live_a && ld_s < nsteps_a;  // the padding step of sweep A
@@ -110,11 +111,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
         const uint16_t* p1 = ld_kind == kDkv ? qp : kp;
         const uint16_t* p2 = ld_kind == kDkv ? dop : vp;
         x1 = *reinterpret_cast<const u32x4*>(p1 + (dead ? 0 : a));
-        x2 = *reinterpret_cast<const u32x4*>(p2 + (dead || ld_kind == kLse ? 0 : a));
+        x2 = *reinterpret_cast<const u32x4*>(p2 + (dead ? 0 : a));
         ++ld_s;
         if (!pad && ++ld_blk == NB) {
             ld_blk = 0;
-            ld_kind = ld_s >= live_a ? kDkv : HASLSE ? kDq : (ld_kind == kLse ? kDq : kLse);
+            ld_kind = ld_s >= live_a ? kDkv : kDq;
         }
     };
     const int t_put = v_chunk_offset<D>(ld_row, ld_col / 8);
@@ -122,10 +123,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
     auto put = [&](const u32x4& x1, const u32x4& x2, int buf, int kind) {
         if (!stager) return;
         *reinterpret_cast<u32x4*>(&rowA[buf][ld_row * G::KSTR + ld_col]) = x1;
-        if (kind != kLse) {
-            *reinterpret_cast<u32x4*>(&trA[buf][t_put]) = t_swap ? u32x4{x1.z, x1.w, x1.x, x1.y} : x1;
-            *reinterpret_cast<u32x4*>(&rowB[buf][ld_row * G::KSTR + ld_col]) = x2;
-        }
+        *reinterpret_cast<u32x4*>(&trA[buf][t_put]) = t_swap ? u32x4{x1.z, x1.w, x1.x, x1.y} : x1;
+        *reinterpret_cast<u32x4*>(&rowB[buf][ld_row * G::KSTR + ld_col]) = x2;
         if (kind == kDkv)
             *reinterpret_cast<u32x4*>(&trB[buf][t_put]) = t_swap ? u32x4{x2.z, x2.w, x2.x, x2.y} : x2;
     };
@@ -187,22 +186,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
 #pragma unroll
     for (int u = 0; u < PD; ++u) issue(sx1[u], sx2[u]);
 
-    // ---- sweep A: per query group, log-sum-exp over K then dQ over K and V ----
+    // ---- sweep A: per query group, dQ over K and V ---------------------------
+    // With the rows' log-sum-exp given, P = exp2(S c - lse) directly.  Without
+    // it, the pass accumulates dQ from unnormalised probabilities exp2(S c - m)
+    // under a running maximum m (refreshed, with dQ and the row sum rescaled,
+    // only when some lane's keys exceed it by the headroom, as in the
+    // forward), and divides by the row sum at the end, where the log-sum-exp
+    // for the key sweep also becomes known: one pass over the keys instead of
+    // two.
+    constexpr float kHeadroom = 8.0f;  // log2 units
     bf16x8 qreg[G::KS], doreg[G::KS];
-    float Dq = 0.0f, m = -INFINITY, l = 0.0f, lse2 = 0.0f;
+    float Dq = 0.0f, m = -INFINITY, lpart = 0.0f, lse2 = 0.0f;
     f32x4 dqacc[G::DT];
     int st = 0;  // step of sweep A
     for (int s0 = 0; s0 < nsteps_a; s0 += PD) {
 #pragma unroll
         for (int u = 0; u < PD; ++u, ++st) {
-            const int per = HASLSE ? NB : 2 * NB;
-            const int grp = st / per, r = st - grp * per;
-            const int kind = (!HASLSE && r < NB) ? kLse : kDq, blk = (!HASLSE && r >= NB) ? r - NB : r;
+            const int grp = st / NB, blk = st - grp * NB;
             const int qt = grp * NW + wave;
             const bool active = st < live_a && qt < ntiles;
-            put(sx1[u], sx2[u], u & 1, kind);
+            put(sx1[u], sx2[u], u & 1, kDq);
             issue(sx1[u], sx2[u]);
-            if (blk == 0 && active && (HASLSE || kind == kLse)) {
+            if (blk == 0 && active) {
                 load_tile(qp, qt, qreg);
                 load_tile(dop, qt, doreg);
                 const int64_t a = row(qt * 16 + li);
@@ -214,28 +219,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                     for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[s][e], (float)o[e], part);
                 }
                 Dq = row_sum4(part);
-                m = -INFINITY;
-                l = 0.0f;
                 if (HASLSE) {
                     lse2 = lse_in[a / D];
                     if (lg == 0 && qt * 16 + li < L) {
                         lse[qt * 16 + li] = lse2;
                         dd[qt * 16 + li] = Dq;
                     }
-#pragma unroll
-                    for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
+                } else {
+                    m = -INFINITY;
+                    lpart = 0.0f;
                 }
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
             }
             __syncthreads();
             if (!active) continue;
-            if (kind == kLse) {
-                // scores S^T (keys x this wave's queries): row maximum and sum of exp2
-                f32x4 sa = zero, sb = zero;
+            // dQ^T += K^T dS^T
+            f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
 #pragma unroll
-                for (int s = 0; s < G::KS; ++s) {
-                    sa = mfma(row_op(rowA[u & 1], 0, s), qreg[s], sa);
-                    sb = mfma(row_op(rowA[u & 1], 1, s), qreg[s], sb);
-                }
+            for (int s = 0; s < G::KS; ++s) {
+                sa = mfma(row_op(rowA[u & 1], 0, s), qreg[s], sa);
+                sb = mfma(row_op(rowA[u & 1], 1, s), qreg[s], sb);
+                pa = mfma(row_op(rowB[u & 1], 0, s), doreg[s], pa);  // dP^T
+                pb = mfma(row_op(rowB[u & 1], 1, s), doreg[s], pb);
+            }
+            if (!HASLSE) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -243,46 +251,42 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                     if (blk * BR + 16 + 4 * lg + i >= L) sb[i] = -INFINITY;
                     mx = fmaxf(mx, fmaxf(sa[i], sb[i]));
                 }
-                const float mnew = fmaxf(m, row_max4(mx) * c_log2);
-                float part = 0.0f;
+                if (__builtin_amdgcn_ballot_w64(mx * c_log2 > m + kHeadroom) != 0) {
+                    const float mnew = fmaxf(m, row_max4(mx) * c_log2);
+                    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+                    lpart *= alpha;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    part += __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -mnew)) +
-                            __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -mnew));
-                l = l * __builtin_amdgcn_exp2f(m - mnew) + row_sum4(part);
-                m = mnew;
-                if (blk == NB - 1) {
+                    for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] *= alpha;
+                    m = mnew;
+                }
+            }
+            const float sub = HASLSE ? lse2 : m;
+            float ds0[4], ds1[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool v0 = blk * BR + 4 * lg + i < L, v1 = blk * BR + 16 + 4 * lg + i < L;
+                const float e0 = v0 ? __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -sub)) : 0.0f;
+                const float e1 = v1 ? __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -sub)) : 0.0f;
+                if (!HASLSE) lpart += e0 + e1;
+                ds0[i] = e0 * (pa[i] - Dq);
+                ds1[i] = e1 * (pb[i] - Dq);
+            }
+            const bf16x8 dsk = pack8(ds0, ds1);
+#pragma unroll
+            for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = mfma(tr_op(trA[u & 1], dt), dsk, dqacc[dt]);
+            if (blk == NB - 1) {
+                float mul = scale;
+                if (!HASLSE) {
+                    // the row's sum over its four lanes; every row has a key, so l >= 1
+                    const float l = row_sum4(lpart);
                     lse2 = m + __builtin_log2f(l);
                     if (lg == 0 && qt * 16 + li < L) {
                         lse[qt * 16 + li] = lse2;
                         dd[qt * 16 + li] = Dq;
                     }
-#pragma unroll
-                    for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
+                    mul = scale / l;
                 }
-            } else {
-                // dQ^T += K^T dS^T
-                f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
-#pragma unroll
-                for (int s = 0; s < G::KS; ++s) {
-                    sa = mfma(row_op(rowA[u & 1], 0, s), qreg[s], sa);
-                    sb = mfma(row_op(rowA[u & 1], 1, s), qreg[s], sb);
-                    pa = mfma(row_op(rowB[u & 1], 0, s), doreg[s], pa);  // dP^T
-                    pb = mfma(row_op(rowB[u & 1], 1, s), doreg[s], pb);
-                }
-                float ds0[4], ds1[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool v0 = blk * BR + 4 * lg + i < L, v1 = blk * BR + 16 + 4 * lg + i < L;
-                    const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -lse2));
-                    const float e1 = __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -lse2));
-                    ds0[i] = v0 ? e0 * (pa[i] - Dq) : 0.0f;
-                    ds1[i] = v1 ? e1 * (pb[i] - Dq) : 0.0f;
-                }
-                const bf16x8 dsk = pack8(ds0, ds1);
-#pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = mfma(tr_op(trA[u & 1], dt), dsk, dqacc[dt]);
-                if (blk == NB - 1) store_rows(dqacc, scale, qt, addq, dqp, qk_f32 != 0);
+                store_rows(dqacc, mul, qt, addq, dqp, qk_f32 != 0);
             }
         }
     }
