@@ -73,6 +73,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                                           const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
                                           uint16_t* yp, float* lse_out, float scale_log2) {
     using G = Geo<D>;
+    constexpr int OPH = QT >= 3 ? 2 : 1;  // parts the K and V operands of a step are read in
     static_assert(PD % 2 == 0, "the LDS buffer of a step must be known at compile time");
     constexpr int QROWS = QSTAGE ? (LMAX + BR - 1) / BR * BR : 1;
     __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][BR * G::KSTR];
@@ -316,19 +317,27 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             s1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         const uint16_t* kb = kbuf[buf];
-        bf16x8 ka0[G::KS], ka1[G::KS];
+        // the K operands in OPH parts (instances of 3+ tiles per wave hold only
+        // half of them at a time, a scheduling barrier between the halves)
 #pragma unroll
-        for (int s = 0; s < G::KS; ++s) {
-            ka0[s] = *reinterpret_cast<const bf16x8*>(&kb[li * G::KSTR + (4 * s + lg) * 8]);
-            ka1[s] = *reinterpret_cast<const bf16x8*>(&kb[(16 + li) * G::KSTR + (4 * s + lg) * 8]);
-        }
+        for (int h = 0; h < OPH; ++h) {
+            constexpr int NS = G::KS / OPH;
+            bf16x8 ka0[NS], ka1[NS];
 #pragma unroll
-        for (int s = 0; s < G::KS; ++s) {
-#pragma unroll
-            for (int t = 0; t < QT; ++t) {
-                s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[s], qreg[t][s], s0[t], 0, 0, 0);
-                s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[s], qreg[t][s], s1[t], 0, 0, 0);
+            for (int i = 0; i < NS; ++i) {
+                const int s = h * NS + i;
+                ka0[i] = *reinterpret_cast<const bf16x8*>(&kb[li * G::KSTR + (4 * s + lg) * 8]);
+                ka1[i] = *reinterpret_cast<const bf16x8*>(&kb[(16 + li) * G::KSTR + (4 * s + lg) * 8]);
             }
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+#pragma unroll
+                for (int t = 0; t < QT; ++t) {
+                    s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[i], qreg[t][h * NS + i], s0[t], 0, 0, 0);
+                    s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[i], qreg[t][h * NS + i], s1[t], 0, 0, 0);
+                }
+            }
+            if (OPH > 1) __builtin_amdgcn_sched_barrier(0);
         }
         const bool mask = ragged && blk == NB - 1;
         const int kbase = blk * BR + 4 * lg;
@@ -376,21 +385,28 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         // +16) at 4 consecutive d (column 4*(dt/2) + li%4, half dt%2); it
         // receives 4 consecutive keys of one d column
         const int vr = v_fetch_row(li, lg);
-        bf16x8 va[G::DT];
 #pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt) {
-            const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
-            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            va[dt] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
-        }
+        for (int t = 0; t < QT; ++t) osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[t], osum[t], 0, 0, 0);
+        // the V operands in OPH parts, as the K operands above
 #pragma unroll
-        for (int t = 0; t < QT; ++t) {
-            osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[t], osum[t], 0, 0, 0);
+        for (int h = 0; h < OPH; ++h) {
+            constexpr int ND = G::DT / OPH;
+            bf16x8 va[ND];
 #pragma unroll
-            for (int dt = 0; dt < G::DT; ++dt)
-                oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pk[t], oacc[t][dt], 0, 0, 0);
+            for (int i = 0; i < ND; ++i) {
+                const int dt = h * ND + i;
+                const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                va[i] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+            }
+#pragma unroll
+            for (int t = 0; t < QT; ++t)
+#pragma unroll
+                for (int i = 0; i < ND; ++i)
+                    oacc[t][h * ND + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pk[t], oacc[t][h * ND + i], 0, 0, 0);
+            if (OPH > 1) __builtin_amdgcn_sched_barrier(0);
         }
     };
 
