@@ -166,7 +166,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     u32x4 sk[PD], sv[PD], sq[PD];
     int ld_it = 0, ld_b = 0;
     // loads of steps past the last problem, and of Q past the last problem,
-    // all read the first 16 bytes of the tensor (one cached line, never used)
+    // all read the first 16 bytes of the tensor (one cached line, never used;
+    // FAST: a descriptor without records, which returns zeros)
     bool ld_dead = nmine <= 0;
     bool q_dead = nmine <= 1;
     Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0, 0, 1};
@@ -333,8 +334,9 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             for (int i = 0; i < NS; ++i) {
 #pragma unroll
                 for (int t = 0; t < QT; ++t) {
-                    s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[i], qreg[t][h * NS + i], s0[t], 0, 0, 0);
-                    s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[i], qreg[t][h * NS + i], s1[t], 0, 0, 0);
+                    const bf16x8 qs = qreg[t][h * NS + i];
+                    s0[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[i], qs, s0[t], 0, 0, 0);
+                    s1[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[i], qs, s1[t], 0, 0, 0);
                 }
             }
             if (OPH > 1) __builtin_amdgcn_sched_barrier(0);
@@ -386,7 +388,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         // receives 4 consecutive keys of one d column
         const int vr = v_fetch_row(li, lg);
 #pragma unroll
-        for (int t = 0; t < QT; ++t) osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[t], osum[t], 0, 0, 0);
+        for (int t = 0; t < QT; ++t)
+            osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[t], osum[t], 0, 0, 0);
         // the V operands in OPH parts, as the K operands above
 #pragma unroll
         for (int h = 0; h < OPH; ++h) {
@@ -405,7 +408,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             for (int t = 0; t < QT; ++t)
 #pragma unroll
                 for (int i = 0; i < ND; ++i)
-                    oacc[t][h * ND + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pk[t], oacc[t][h * ND + i], 0, 0, 0);
+                    oacc[t][h * ND + i] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[i], pk[t], oacc[t][h * ND + i], 0, 0, 0);
             if (OPH > 1) __builtin_amdgcn_sched_barrier(0);
         }
     };
