@@ -196,12 +196,16 @@ squad_status_t squad_window_solve(int T, int Hs, int Ws, int* wt, int* wh, int* 
  * receive dL/dq, dL/dk, dL/dv.  All [B, n, heads, d] of one dtype, as for
  * squad_attn_fwd (windows must tile the grid).  workspace: device buffer of at
  * least squad_attn_bwd_workspace_bytes(...) bytes, 16-byte aligned: the
- * recomputed local output Y and dY in the dtype, float32 partial dq, dk and,
- * in bf16, the float32 log-sum-exp of Y's rows (which the local pass's
- * backward reuses instead of recomputing it) (contents on entry ignored; one
- * workspace must not serve calls that may run at the same time).  Three kernels are enqueued on `stream`: the local pass
- * (recomputing Y), the global pass's backward, the local pass's backward.
- * P and dS enter the bf16 MFMAs rounded to bf16; sums are float32.
+ * recomputed local output Y, dY and the global pass's dq, dk contributions,
+ * all in the dtype, and, in bf16, float32 per row of Y: its log-sum-exp
+ * (which the local pass's backward reuses instead of recomputing it) and
+ * D = rowsum(dY * Y) (which the global pass's backward computes from what it
+ * holds, so the local pass's backward does not read Y) (contents on entry
+ * ignored; one workspace must not serve calls that may run at the same
+ * time).  Three kernels are enqueued on `stream`: the local pass (recomputing
+ * Y), the global pass's backward, the local pass's backward.  In bf16, P and
+ * dS enter the MFMAs rounded to bf16 and the global pass's dq, dk
+ * contributions are stored in bf16; sums are float32.
  *
  * Errors as squad_attn_fwd for the shape, dtype and sizes; SQUAD_ERR_NULL for
  * any NULL tensor; SQUAD_ERR_WORKSPACE for a NULL or too small workspace;
@@ -234,10 +238,12 @@ double squad_attn_bwd_flops(int B, int heads, int T, int Hs, int Ws,
                             int wt, int wh, int ww, int d);
 
 /* HBM bytes of one squad_attn_bwd call as its three kernels move them:
- * E*sizeof(dtype)*18 + E*16 with E = B*n*heads*d (recompute of Y: 3 reads, 1
- * write; global backward: q, k, Y, O, dO read, dY written, float32 dq, dk
- * written; local backward: q, k, v, Y, dY read, float32 partials read, dq, dk,
- * dv written).  -1 on a rejected shape or dtype.  Pure host function. */
+ * E*sizeof(dtype)*21 in bf16 and E*sizeof(dtype)*22 in float32, with
+ * E = B*n*heads*d (recompute of Y: 3 reads, 1 write; global backward: q, k,
+ * Y, O, dO read, dY and the dq, dk contributions written; local backward: q,
+ * k, v, dY and the contributions read, and Y in float32 only, dq, dk, dv
+ * written; the per-row float32 arrays are not counted).  -1 on a rejected
+ * shape or dtype.  Pure host function. */
 double squad_attn_bwd_bytes(int B, int heads, int T, int Hs, int Ws,
                             int wt, int wh, int ww, int d, int dtype);
 

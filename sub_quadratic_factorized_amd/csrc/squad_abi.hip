@@ -229,12 +229,12 @@ hipError_t run_two_passes(const Problem& pr, bool local_first, const void* q, co
     return e;
 }
 
-// Workspace of the backward: Y (the recomputed local output) and dY in the
-// dtype, then the global pass's float32 contributions to dQ and dK, then the
-// local pass's row log-sum-exp (float32, B*n*heads; bf16 only); each region
-// starts on a 256-byte boundary.
+// Workspace of the backward: Y (the recomputed local output), dY and the
+// global pass's contributions to dQ and dK, all in the dtype, then (bf16 only)
+// the local pass's rows' log-sum-exp and D, float32 [B, n, heads] each; every
+// region starts on a 256-byte boundary.
 struct BwdLayout {
-    size_t y, dy, gq, gk, lse, total;
+    size_t y, dy, gq, gk, lse, dl, total;
 };
 
 BwdLayout bwd_layout(const Problem& pr) {
@@ -244,9 +244,11 @@ BwdLayout bwd_layout(const Problem& pr) {
     l.y = 0;
     l.dy = up(e * esize(pr.dtype));
     l.gq = l.dy + up(e * esize(pr.dtype));
-    l.gk = l.gq + up(e * 4);
-    l.lse = l.gk + up(e * 4);
-    l.total = l.lse + (pr.dtype == SQUAD_BF16 ? up(e / pr.d * 4) : 0);
+    l.gk = l.gq + up(e * esize(pr.dtype));
+    l.lse = l.gk + up(e * esize(pr.dtype));
+    const size_t rows = pr.dtype == SQUAD_BF16 ? up(e / pr.d * 4) : 0;
+    l.dl = l.lse + rows;
+    l.total = l.dl + rows;
     return l;
 }
 
@@ -293,23 +295,25 @@ hipError_t run_backward(const Problem& pr, const void* q, const void* k, const v
     const BwdLayout lay = bwd_layout(pr);
     char* w = static_cast<char*>(ws);
     void *y = w + lay.y, *dy = w + lay.dy;
-    float *gq = reinterpret_cast<float*>(w + lay.gq), *gk = reinterpret_cast<float*>(w + lay.gk);
+    void *gq = w + lay.gq, *gk = w + lay.gk;
     const bool bf16 = pr.dtype == SQUAD_BF16;
     float* lse = bf16 ? reinterpret_cast<float*>(w + lay.lse) : nullptr;
+    float* dl = bf16 ? reinterpret_cast<float*>(w + lay.dl) : nullptr;
     // the forward keeps only O: recompute the local output Y (and, in bf16,
     // its rows' log-sum-exp, which the local pass's backward then reuses)
     const PassGeom gy = make_geom(pr, false);
     hipError_t e = bf16 ? launch_pass_bf16(gy, pr.d, q, k, v, y, nullptr, lse, st)
                         : launch_pass_f32(gy, pr.d, q, k, v, y, nullptr, st);
     if (e != hipSuccess) return e;
-    // global pass (values Y, output O): dQ, dK contributions in float32, dY
+    // global pass (values Y, output O): its dQ, dK contributions, dY and, in
+    // bf16, the local pass's D = rowsum(dY * Y)
     const PassGeom gg = make_geom(pr, true);
-    BwdArgs ag{q, k, y, out, dout, nullptr, nullptr, gq, gk, dy, true, nullptr};
+    BwdArgs ag{q, k, y, out, dout, nullptr, nullptr, gq, gk, dy, nullptr, nullptr, dl};
     e = bf16 ? launch_bwd_pass_bf16(gg, pr.d, ag, st) : launch_bwd_pass_f32(gg, pr.d, ag, st);
     if (e != hipSuccess) return e;
     // local pass (values V, output Y, upstream dY): adds the global pass's share
     const PassGeom gl = make_geom(pr, false);
-    BwdArgs al{q, k, v, y, dy, gq, gk, dq, dk, dv, !bf16, lse};
+    BwdArgs al{q, k, v, y, dy, gq, gk, dq, dk, dv, lse, dl, nullptr};
     return bf16 ? launch_bwd_pass_bf16(gl, pr.d, al, st) : launch_bwd_pass_f32(gl, pr.d, al, st);
 }
 
@@ -536,10 +540,11 @@ double squad_attn_bwd_bytes(int B, int heads, int T, int Hs, int Ws, int wt, int
     if (squad::check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1.0;
     if (empty) return 0.0;
     const double e = (double)pr.elems, es = squad::esize(dtype);
-    // recompute Y: 3 reads + 1 write; global pass: q, k, Y, O, dO read, dY
-    // written, float32 dQ and dK written; local pass: q, k, v, Y, dY and the
-    // float32 partials read, dq, dk, dv written
-    return e * es * (4.0 + 6.0 + 8.0) + e * 4.0 * 4.0;
+    // recompute Y: 3 reads + 1 write; global pass: q, k, Y, O, dO read, dY and
+    // the dQ, dK contributions written; local pass: q, k, v, dY and the
+    // contributions read (and Y, for D, in float32 only), dq, dk, dv written
+    // (per-row float32 log-sum-exp and D not counted)
+    return e * es * (4.0 + 8.0 + (dtype == SQUAD_BF16 ? 9.0 : 10.0));
 }
 
 squad_status_t squad_attn_check(const void* q, const void* k, const void* v, const void* out, int B, int heads,

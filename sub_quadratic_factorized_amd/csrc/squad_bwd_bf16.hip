@@ -20,15 +20,18 @@
 //     operand is a block read transposed (the V layout and ds_read_b64_tr_b16
 //     fetch of the forward kernel), the B operand is a 16x16 result tile pair
 //     of the first kind packed to bf16 (its rows are the contracted tokens).
-// Query sweep (waves own 16-query tiles): D from dO and O, then one pass over
-// K and V accumulating dQ^T; when the rows' log-sum-exp is given (HASLSE: the
-// local pass, whose forward the backward has just recomputed) P is formed from
-// it, otherwise dQ^T accumulates unnormalised probabilities under a running
-// maximum and is divided by the row sum at the end of the pass, which also
-// yields the log-sum-exp.  Key sweep (waves own 16-key tiles): a pass over Q
-// and dO accumulating dV^T and dK^T from P and dS recomputed with the stored
-// log-sum-exp and D.  P and dS enter their MFMAs rounded to bf16; all sums are
-// float32.
+// Query sweep (waves own 16-query tiles): D from dO and O (or given per row:
+// then O is not read), then one pass over K and V accumulating dQ^T; when the
+// rows' log-sum-exp is given (HASLSE: the local pass, whose forward the
+// backward has just recomputed) P is formed from it, otherwise dQ^T
+// accumulates unnormalised probabilities under a running maximum and is
+// divided by the row sum at the end of the pass, which also yields the
+// log-sum-exp.  Key sweep (waves own 16-key tiles): a pass over Q and dO
+// accumulating dV^T and dK^T from P and dS recomputed with the stored
+// log-sum-exp and D, and optionally rowsum(dV * V) of the values rows (D of
+// the backward of the pass that produced the values, which then need not read
+// them again).  P and dS enter their MFMAs rounded to bf16, and the other
+// pass's contributions to dQ and dK arrive in bf16; all sums are float32.
 #include "squad_internal.h"
 #include "squad_layout.h"
 #include "squad_mfma.h"
@@ -58,9 +61,10 @@ __device__ __forceinline__ bf16x8 pack8(const float (&lo)[4], const float (&hi)[
 template <int D, bool HASLSE, int NW, int PD>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : 2))) void squad_bwd_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
-    const uint16_t* __restrict__ op, const uint16_t* __restrict__ dop, const float* __restrict__ addq,
-    const float* __restrict__ addk, void* __restrict__ dqp, void* __restrict__ dkp, uint16_t* __restrict__ dvp,
-    const float* __restrict__ lse_in, int qk_f32, float c_log2, float scale) {
+    const uint16_t* __restrict__ op, const uint16_t* __restrict__ dop, const uint16_t* __restrict__ addq,
+    const uint16_t* __restrict__ addk, uint16_t* __restrict__ dqp, uint16_t* __restrict__ dkp,
+    uint16_t* __restrict__ dvp, const float* __restrict__ lse_in, const float* __restrict__ dd_in,
+    float* __restrict__ vdot, float c_log2, float scale) {
     using G = BlockGeo<D>;
     __shared__ __attribute__((aligned(16))) uint16_t rowA[2][BR * G::KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t rowB[2][BR * G::KSTR];
@@ -146,9 +150,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
         return __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
     };
     // a transposed accumulator (rows d as the forward output tiles, column =
-    // token li of `tile`) times `mul`, plus an optional float32 addend, stored
+    // token li of `tile`) times `mul`, plus an optional bf16 addend, stored
     // to the token's row (8 consecutive d per lane and tile pair)
-    auto store_rows = [&](const f32x4 (&acc)[G::DT], float mul, int tile, const float* add, void* dst, bool f32) {
+    auto store_rows = [&](const f32x4 (&acc)[G::DT], float mul, int tile, const uint16_t* add, uint16_t* dst) {
         const int r = tile * 16 + li;
         if (r >= L) return;
         const int64_t a = row(r) + 8 * lg;
@@ -161,24 +165,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                 o[4 + i] = acc[2 * p + 1][i] * mul;
             }
             if (add) {
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(add + a + 32 * p);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(add + a + 32 * p + 4);
+                const bf16x8 x = *reinterpret_cast<const bf16x8*>(add + a + 32 * p);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    o[i] += x0[i];
-                    o[4 + i] += x1[i];
-                }
+                for (int e = 0; e < 8; ++e) o[e] += (float)x[e];
             }
-            if (f32) {
-                float* d32 = static_cast<float*>(dst) + a + 32 * p;
-                *reinterpret_cast<f32x4*>(d32) = f32x4{o[0], o[1], o[2], o[3]};
-                *reinterpret_cast<f32x4*>(d32 + 4) = f32x4{o[4], o[5], o[6], o[7]};
-            } else {
-                bf16x8 b;
+            bf16x8 b;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) b[e] = static_cast<__bf16>(o[e]);
-                *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(dst) + a + 32 * p) = b;
-            }
+            for (int e = 0; e < 8; ++e) b[e] = static_cast<__bf16>(o[e]);
+            *reinterpret_cast<bf16x8*>(dst + a + 32 * p) = b;
         }
     };
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -211,14 +205,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                 load_tile(qp, qt, qreg);
                 load_tile(dop, qt, doreg);
                 const int64_t a = row(qt * 16 + li);
-                float part = 0.0f;
+                if (dd_in) {
+                    Dq = dd_in[a / D];
+                } else {
+                    float part = 0.0f;
 #pragma unroll
-                for (int s = 0; s < G::KS; ++s) {
-                    const bf16x8 o = *reinterpret_cast<const bf16x8*>(op + a + (4 * s + lg) * 8);
+                    for (int s = 0; s < G::KS; ++s) {
+                        const bf16x8 o = *reinterpret_cast<const bf16x8*>(op + a + (4 * s + lg) * 8);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[s][e], (float)o[e], part);
+                        for (int e = 0; e < 8; ++e) part = fmaf((float)doreg[s][e], (float)o[e], part);
+                    }
+                    Dq = row_sum4(part);
                 }
-                Dq = row_sum4(part);
                 if (HASLSE) {
                     lse2 = lse_in[a / D];
                     if (lg == 0 && qt * 16 + li < L) {
@@ -286,7 +284,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                     }
                     mul = scale / l;
                 }
-                store_rows(dqacc, mul, qt, addq, dqp, qk_f32 != 0);
+                store_rows(dqacc, mul, qt, addq, dqp);
             }
         }
     }
@@ -339,8 +337,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                 dkacc[dt] = mfma(tr_op(trA[u & 1], dt), dsp, dkacc[dt]);
             }
             if (qb == NB - 1) {
-                store_rows(dkacc, scale, kt, addk, dkp, qk_f32 != 0);
-                store_rows(dvacc, 1.0f, kt, nullptr, dvp, false);
+                store_rows(dkacc, scale, kt, addk, dkp);
+                store_rows(dvacc, 1.0f, kt, nullptr, dvp);
+                if (vdot) {
+                    // rowsum(dV * V) of the tile's rows, dV rounded as stored:
+                    // accumulator pair p holds d = 32p + 8lg .. +7 of row li,
+                    // the columns of vreg[p]
+                    float part = 0.0f;
+#pragma unroll
+                    for (int p = 0; p < D / 32; ++p)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            part = fmaf((float)static_cast<__bf16>(dvacc[2 * p][i]), (float)vreg[p][i], part);
+                            part = fmaf((float)static_cast<__bf16>(dvacc[2 * p + 1][i]), (float)vreg[p][4 + i], part);
+                        }
+                    const float dsum = row_sum4(part);
+                    const int r = kt * 16 + li;
+                    if (lg == 0 && r < L) vdot[row(r) / D] = dsum;
+                }
             }
         }
     }
@@ -353,8 +367,10 @@ hipError_t launch_nw(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((squad_bwd_pass_bf16<D, HASLSE, NW, PD>), dim3(g.nprob), dim3(64 * NW), 0, st, g,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.vals), static_cast<const uint16_t*>(a.out),
-                       static_cast<const uint16_t*>(a.dout), a.addq, a.addk, a.dq, a.dk,
-                       static_cast<uint16_t*>(a.dvals), a.lse, a.qk_f32 ? 1 : 0, c_log2, scale);
+                       static_cast<const uint16_t*>(a.dout), static_cast<const uint16_t*>(a.addq),
+                       static_cast<const uint16_t*>(a.addk), static_cast<uint16_t*>(a.dq),
+                       static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dvals), a.lse, a.dd_in, a.vdot,
+                       c_log2, scale);
     return hipGetLastError();
 }
 

@@ -149,6 +149,7 @@ hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd_pass_f32(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream) {
+    if (a.lse || a.dd_in || a.vdot) return hipErrorInvalidValue;  // bf16 kernels only
     if (d == 128) return launch_d<128>(g, a, stream);
     return launch_d<64>(g, a, stream);
 }

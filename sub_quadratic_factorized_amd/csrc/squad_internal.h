@@ -173,16 +173,22 @@ hipError_t launch_pass_f32(const PassGeom& g, int d, const void* q, const void* 
 
 // Operands of one pass's backward (unpadded grids).  q, k, vals: the pass's
 // inputs; out: its output O; dout: the upstream gradient dO.  The kernels
-// write dQ and dK (plus addq / addk when those are not null: float32
-// contributions of the other pass) and dV of the values.  In the bf16 kernels
-// q, k, vals, out, dout and dvals are bf16 and dq, dk are float32 when qk_f32,
-// else bf16; in the float32 kernels everything is float32.
+// write dQ and dK (plus addq / addk when those are not null: the other pass's
+// contributions, in the kernels' dtype) and dV of the values.  The bf16
+// kernels read and write bf16 tensors, with float32 sums inside; the float32
+// kernels are float32 throughout.  bf16 only, each may be null (the float32
+// kernels take neither): lse, the rows' log-sum-exp as launch_pass_bf16
+// writes it; dd_in, the rows' D = rowsum(dO * O) (then `out` is not read);
+// vdot, receives rowsum(dV * V) of every values row (dV as stored), which is
+// D for the backward of the pass that produced the values.  The per-row
+// arrays are [B, n, heads] float32.
 struct BwdArgs {
     const void *q, *k, *vals, *out, *dout;
-    const float *addq, *addk;
+    const void *addq, *addk;
     void *dq, *dk, *dvals;
-    bool qk_f32;
-    const float* lse;  // bf16 only, may be null: the rows' log-sum-exp as launch_pass_bf16 writes it
+    const float* lse;
+    const float* dd_in;
+    float* vdot;
 };
 
 hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream);

@@ -278,7 +278,7 @@ def test_window_solver_matches_oracle_rule():
 DO, DQ, DK, DV = A + 16 * BYTES, A + 20 * BYTES, A + 24 * BYTES, A + 28 * BYTES
 BWS = A + 32 * BYTES
 # Y and dY in bf16, float32 dq and dk partials, float32 row log-sum-exp (256-byte rounded: exact here)
-BWS_BYTES = 2 * BYTES + 2 * 2 * BYTES + 18480 * 24 * 4
+BWS_BYTES = 4 * BYTES + 2 * 18480 * 24 * 4
 
 
 def bcall(fn="check", q=Q, k=K, v=V, out=O, dout=DO, dq=DQ, dk=DK, dv=DV, ws=BWS, ws_bytes=BWS_BYTES,
@@ -300,7 +300,8 @@ def test_bwd_workspace_and_helpers():
     assert bd.squad_attn_bwd_flops(*GEO.values()) == 2.5 * 63_128_862_720
     assert bd.squad_attn_bwd_flops(*GEO.values()) == so.squad_backward_flops(*GEO.values())
     e = 18480 * 24 * 128
-    assert bd.squad_attn_bwd_bytes(*GEO.values(), bd.SQUAD_BF16) == e * 2 * 18 + e * 16
+    assert bd.squad_attn_bwd_bytes(*GEO.values(), bd.SQUAD_BF16) == e * 2 * 21
+    assert bd.squad_attn_bwd_bytes(*GEO.values(), bd.SQUAD_F32) == e * 4 * 22
 
 
 @pytest.mark.parametrize("fn", ["check", "bwd"])
