@@ -218,6 +218,43 @@ squad_status_t squad_attn_bwd(const void* q, const void* k, const void* v, const
                               int wt, int wh, int ww, int d,
                               int dtype, hipStream_t stream);
 
+/* squad_attn_fwd for training: the same two kernels and the same `out` (bit
+ * for bit), and the local pass's output Y, which squad_attn_fwd keeps only
+ * inside `out`, written to `y` instead (the global pass then reads its values
+ * from `y`), plus, in bf16, the log-sum-exp of Y's rows to `lse` ([B, n,
+ * heads] float32, in log2 units of the scores scaled by log2(e)/sqrt(d)), so
+ * that squad_attn_bwd_saved need not recompute them.  Same HBM traffic as
+ * squad_attn_fwd (the extra lse is 1/(2d) of a tensor).  y: [B, n, heads, d]
+ * in the dtype.  Errors as squad_attn_fwd; then SQUAD_ERR_NULL for a NULL y
+ * (or lse in bf16; lse is ignored in float32), SQUAD_ERR_ALIGN for y or lse
+ * not 16-byte aligned, SQUAD_ERR_ALIAS if y or lse overlaps q, k, v, out or
+ * each other.  Two kernels on `stream`. */
+squad_status_t squad_attn_fwd_save(const void* q, const void* k, const void* v, void* out, void* y, float* lse,
+                                   int B, int heads, int T, int Hs, int Ws,
+                                   int wt, int wh, int ww, int d,
+                                   int dtype, hipStream_t stream);
+
+/* squad_attn_bwd from the activations squad_attn_fwd_save kept (y, and lse in
+ * bf16; both unchanged since) instead of recomputing them: the same two
+ * backward kernels and the same gradients bit for bit, without the local
+ * pass's recomputation.  workspace: at least
+ * squad_attn_bwd_saved_workspace_bytes(...) bytes (dY and the global pass's
+ * dq, dk contributions, and in bf16 the local pass's D).  Errors as
+ * squad_attn_bwd; SQUAD_ERR_NULL, SQUAD_ERR_ALIGN for y and lse as for the
+ * tensors; SQUAD_ERR_ALIAS also if y or lse overlaps a gradient or the
+ * workspace. */
+squad_status_t squad_attn_bwd_saved(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                    const void* y, const float* lse, void* dq, void* dk, void* dv,
+                                    void* workspace, size_t workspace_bytes,
+                                    int B, int heads, int T, int Hs, int Ws,
+                                    int wt, int wh, int ww, int d,
+                                    int dtype, hipStream_t stream);
+
+/* Bytes of workspace squad_attn_bwd_saved needs (0 for an empty problem, -1
+ * on a shape or dtype it rejects).  Pure host function. */
+long long squad_attn_bwd_saved_workspace_bytes(int B, int heads, int T, int Hs, int Ws,
+                                               int wt, int wh, int ww, int d, int dtype);
+
 /* Validation only for squad_attn_bwd (pure host function). */
 squad_status_t squad_attn_check_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                                     const void* dq, const void* dk, const void* dv,
@@ -279,7 +316,8 @@ const char* squad_status_str(int status);
 int squad_attn_last_hip_error(void);
 
 /* Version of this ABI (bumped on any change; 2 adds the padded entry points,
- * the backward and SQUAD_ERR_WORKSPACE). */
+ * the backward and SQUAD_ERR_WORKSPACE; 3 the saved-activation forward and
+ * backward). */
 int squad_attn_abi_version(void);
 
 #ifdef __cplusplus

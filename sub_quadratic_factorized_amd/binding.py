@@ -34,7 +34,7 @@ ALL_SYMBOLS = COMPUTE_ENTRY_POINTS + (
     "squad_attn_fwd_padded", "squad_attn_check_padded", "squad_attn_padded_workspace_bytes",
     "squad_attn_flops_padded", "squad_attn_bytes_padded", "squad_window_solve",
     "squad_attn_bwd", "squad_attn_check_bwd", "squad_attn_bwd_workspace_bytes", "squad_attn_bwd_flops",
-    "squad_attn_bwd_bytes",
+    "squad_attn_bwd_bytes", "squad_attn_fwd_save", "squad_attn_bwd_saved", "squad_attn_bwd_saved_workspace_bytes",
     "squad_attn_check", "squad_attn_max_len", "squad_attn_flops", "squad_attn_bytes", "squad_status_str",
     "squad_attn_last_hip_error", "squad_attn_abi_version",
 )
@@ -85,6 +85,12 @@ def lib() -> ctypes.CDLL:
     L.squad_attn_check_bwd.restype = i
     L.squad_attn_bwd_workspace_bytes.argtypes = [i] * 10
     L.squad_attn_bwd_workspace_bytes.restype = ctypes.c_longlong
+    L.squad_attn_fwd_save.argtypes = [p] * 6 + [i] * 10 + [p]
+    L.squad_attn_fwd_save.restype = i
+    L.squad_attn_bwd_saved.argtypes = [p] * 11 + [sz] + [i] * 10 + [p]
+    L.squad_attn_bwd_saved.restype = i
+    L.squad_attn_bwd_saved_workspace_bytes.argtypes = [i] * 10
+    L.squad_attn_bwd_saved_workspace_bytes.restype = ctypes.c_longlong
     L.squad_attn_bwd_flops.argtypes = [i] * 9
     L.squad_attn_bwd_flops.restype = d
     L.squad_attn_bwd_bytes.argtypes = [i] * 10
@@ -158,6 +164,10 @@ def squad_attn_bytes_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> float:
 
 def squad_attn_bwd_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> int:
     return lib().squad_attn_bwd_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
+
+
+def squad_attn_bwd_saved_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype) -> int:
+    return lib().squad_attn_bwd_saved_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dtype)
 
 
 def squad_attn_bwd_flops(B, heads, T, Hs, Ws, wt, wh, ww, d) -> float:
@@ -309,4 +319,85 @@ def squad_attn_bwd(q, k, v, out, dout, grid, window, dq=None, dk=None, dv=None, 
                                   B, heads, T, Hs, Ws, wt, wh, ww, d, dt, stream)
     if st != SQUAD_OK:
         raise SquadError(st, "squad_attn_bwd")
+    return dq, dk, dv
+
+
+def _like(t, ref, what):
+    if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous tensor like q")
+
+
+def _lse_like(t, q):
+    import torch
+    B, n, heads, _ = q.shape
+    if t.shape != (B, n, heads) or t.dtype != torch.float32 or t.device != q.device or not t.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, n, heads] tensor on q's device")
+
+
+def squad_attn_fwd_save(q, k, v, grid, window, out=None, y=None, lse=None, stream=None):
+    """(out, y, lse): squad_attn_fwd's output, the local pass's output Y and,
+    in bf16, its rows' log-sum-exp (None in float32), kept for
+    squad_attn_bwd_saved."""
+    import torch
+    out = _check_tensors(q, k, v, out, grid)
+    B, n, heads, d = q.shape
+    T, Hs, Ws = grid
+    wt, wh, ww = window
+    dt = _dtype_code(q)
+    y = torch.empty_like(q) if y is None else y
+    _like(y, q, "y")
+    if dt == SQUAD_BF16:
+        lse = torch.empty(B, n, heads, dtype=torch.float32, device=q.device) if lse is None else lse
+        _lse_like(lse, q)
+    else:
+        lse = None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().squad_attn_fwd_save(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), y.data_ptr(),
+                                       lse.data_ptr() if lse is not None else None, B, heads, T, Hs, Ws, wt, wh, ww,
+                                       d, dt, stream)
+    if st != SQUAD_OK:
+        raise SquadError(st, "squad_attn_fwd_save")
+    return out, y, lse
+
+
+def squad_attn_bwd_saved(q, k, v, out, dout, y, lse, grid, window, dq=None, dk=None, dv=None, workspace=None,
+                         stream=None):
+    """(dq, dk, dv) as squad_attn_bwd, from the Y (and bf16 lse) that
+    squad_attn_fwd_save kept.  `workspace`: at least
+    squad_attn_bwd_saved_workspace_bytes bytes (allocated through torch if
+    None)."""
+    import torch
+    _check_tensors(q, k, v, None, grid)
+    for t, what in ((out, "out"), (dout, "dout"), (y, "y")):
+        _like(t, q, what)
+    dt = _dtype_code(q)
+    if dt == SQUAD_BF16:
+        if lse is None:
+            raise ValueError("lse is required in bf16")
+        _lse_like(lse, q)
+    dq, dk, dv = (torch.empty_like(q) if t is None else t for t in (dq, dk, dv))
+    for t, what in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _like(t, q, what)
+    B, n, heads, d = q.shape
+    T, Hs, Ws = grid
+    wt, wh, ww = window
+    need = squad_attn_bwd_saved_workspace_bytes(B, heads, T, Hs, Ws, wt, wh, ww, d, dt)
+    if need < 0:
+        raise SquadError(SQUAD_ERR_SHAPE, "squad_attn_bwd_saved")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().squad_attn_bwd_saved(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                        y.data_ptr(), lse.data_ptr() if lse is not None else None, dq.data_ptr(),
+                                        dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, heads, T,
+                                        Hs, Ws, wt, wh, ww, d, dt, stream)
+    if st != SQUAD_OK:
+        raise SquadError(st, "squad_attn_bwd_saved")
     return dq, dk, dv

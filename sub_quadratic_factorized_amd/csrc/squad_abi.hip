@@ -229,36 +229,80 @@ hipError_t run_two_passes(const Problem& pr, bool local_first, const void* q, co
     return e;
 }
 
-// Workspace of the backward: Y (the recomputed local output), dY and the
-// global pass's contributions to dQ and dK, all in the dtype, then (bf16 only)
-// the local pass's rows' log-sum-exp and D, float32 [B, n, heads] each; every
-// region starts on a 256-byte boundary.
+// Workspace of the backward: Y (the recomputed local output; not with saved
+// activations), dY and the global pass's contributions to dQ and dK, all in
+// the dtype, then (bf16 only) the local pass's rows' log-sum-exp (not with
+// saved activations) and D, float32 [B, n, heads] each; every region starts on
+// a 256-byte boundary.
 struct BwdLayout {
     size_t y, dy, gq, gk, lse, dl, total;
 };
 
-BwdLayout bwd_layout(const Problem& pr) {
+BwdLayout bwd_layout(const Problem& pr, bool saved) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t e = (size_t)pr.elems;
+    const size_t e = (size_t)pr.elems, t = up(e * esize(pr.dtype));
+    const bool bf16 = pr.dtype == SQUAD_BF16;
+    const size_t rows = bf16 ? up(e / pr.d * 4) : 0;
     BwdLayout l;
-    l.y = 0;
-    l.dy = up(e * esize(pr.dtype));
-    l.gq = l.dy + up(e * esize(pr.dtype));
-    l.gk = l.gq + up(e * esize(pr.dtype));
-    l.lse = l.gk + up(e * esize(pr.dtype));
-    const size_t rows = pr.dtype == SQUAD_BF16 ? up(e / pr.d * 4) : 0;
-    l.dl = l.lse + rows;
-    l.total = l.dl + rows;
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        const size_t p = at;
+        at += bytes;
+        return p;
+    };
+    l.y = saved ? 0 : take(t);
+    l.dy = take(t);
+    l.gq = take(t);
+    l.gk = take(t);
+    l.lse = saved ? 0 : take(rows);
+    l.dl = take(rows);
+    l.total = at;
     return l;
 }
 
+// The activations squad_attn_fwd_save keeps: y as q ([B, n, heads, d] in the
+// dtype) and, in bf16, lse ([B, n, heads] float32).  Both non-NULL (lse in bf16
+// only), 16-byte aligned, and overlapping none of `tensors` (a forward's
+// output, or a backward's gradients) nor each other.
+squad_status_t check_saved(const Problem& pr, const void* y, const void* lse, const void* const* tensors, int ntensors) {
+    const bool bf16 = pr.dtype == SQUAD_BF16;
+    if (!y || (bf16 && !lse)) return SQUAD_ERR_NULL;
+    if (((uintptr_t)y | (bf16 ? (uintptr_t)lse : 0)) & 15u) return SQUAD_ERR_ALIGN;
+    const size_t lse_bytes = (size_t)pr.elems / (size_t)pr.d * 4;
+    for (int i = 0; i < ntensors; ++i) {
+        if (overlaps(y, tensors[i], pr.bytes)) return SQUAD_ERR_ALIAS;
+        if (bf16) {
+            const uintptr_t a = (uintptr_t)lse, b = (uintptr_t)tensors[i];
+            if (a < b + pr.bytes && b < a + lse_bytes) return SQUAD_ERR_ALIAS;
+        }
+    }
+    if (bf16) {
+        const uintptr_t a = (uintptr_t)lse, b = (uintptr_t)y;
+        if (a < b + pr.bytes && b < a + lse_bytes) return SQUAD_ERR_ALIAS;
+    }
+    return SQUAD_OK;
+}
+
+// Arguments of squad_attn_fwd_save: the forward's checks, then y and lse,
+// which must not overlap q, k, v or out.
+squad_status_t validate_save(const void* q, const void* k, const void* v, const void* out, const void* y,
+                             const void* lse, int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d,
+                             int dtype, Problem* pr, bool* empty) {
+    const squad_status_t s = validate(q, k, v, out, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, pr, empty);
+    if (s != SQUAD_OK || *empty) return s;
+    const void* others[4] = {q, k, v, out};
+    return check_saved(*pr, y, lse, others, 4);
+}
+
 // Arguments of squad_attn_bwd: the forward's checks on (q, k, v, out), then
-// dout and the three gradients, then the workspace; gradients must not overlap
-// any input, one another or the workspace.
+// dout and the three gradients, then (saved activations) y and lse, then the
+// workspace; gradients must not overlap any input, one another or the
+// workspace, and the saved activations must not overlap the gradients or the
+// workspace.
 squad_status_t validate_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                             const void* dq, const void* dk, const void* dv, const void* ws, size_t ws_size, int B,
                             int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype, Problem* pr,
-                            bool* empty) {
+                            bool* empty, bool saved = false, const void* y = nullptr, const void* lse = nullptr) {
     squad_status_t s = check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, pr, empty);
     if (s != SQUAD_OK) return s;
     if (*empty) return SQUAD_OK;
@@ -268,12 +312,17 @@ squad_status_t validate_bwd(const void* q, const void* k, const void* v, const v
     if (pr->m > maxlen || pr->nw > maxlen) return SQUAD_ERR_UNSUPPORTED;
     pr->dtype = dtype;
     if (!q || !k || !v || !out || !dout || !dq || !dk || !dv) return SQUAD_ERR_NULL;
-    const BwdLayout lay = bwd_layout(*pr);
+    pr->bytes = (size_t)pr->elems * (size_t)esize(dtype);
+    if (saved) {
+        const void* grads[3] = {dq, dk, dv};
+        const squad_status_t s2 = check_saved(*pr, y, lse, grads, 3);
+        if (s2 != SQUAD_OK) return s2;
+    }
+    const BwdLayout lay = bwd_layout(*pr, saved);
     if (!ws || ws_size < lay.total) return SQUAD_ERR_WORKSPACE;
     const uintptr_t bits = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout |
                            (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)ws;
     if (bits & 15u) return SQUAD_ERR_ALIGN;
-    pr->bytes = (size_t)pr->elems * (size_t)esize(dtype);
     const void* grads[3] = {dq, dk, dv};
     const void* ins[5] = {q, k, v, out, dout};
     const uintptr_t w0 = (uintptr_t)ws, w1 = w0 + lay.total;
@@ -287,24 +336,47 @@ squad_status_t validate_bwd(const void* q, const void* k, const void* v, const v
         const uintptr_t a = (uintptr_t)t;
         if (a < w1 && w0 < a + pr->bytes) return SQUAD_ERR_ALIAS;
     }
+    if (saved) {
+        const uintptr_t a = (uintptr_t)y;
+        if (a < w1 && w0 < a + pr->bytes) return SQUAD_ERR_ALIAS;
+        const uintptr_t b = (uintptr_t)lse;
+        if (dtype == SQUAD_BF16 && b < w1 && w0 < b + (size_t)pr->elems / (size_t)d * 4) return SQUAD_ERR_ALIAS;
+    }
     return SQUAD_OK;
 }
 
+// The local pass into y (in bf16 also its rows' log-sum-exp into lse).
+hipError_t run_local_saving(const Problem& pr, const void* q, const void* k, const void* v, void* y, float* lse,
+                            hipStream_t st) {
+    const PassGeom g = make_geom(pr, false);
+    if (pr.dtype == SQUAD_BF16) return launch_pass_bf16(g, pr.d, q, k, v, y, nullptr, lse, st);
+    return launch_pass_f32(g, pr.d, q, k, v, y, nullptr, st);
+}
+
+// The backward's three kernels, or two when the caller passes the local
+// output Y (and in bf16 its rows' log-sum-exp) that squad_attn_fwd_save kept.
 hipError_t run_backward(const Problem& pr, const void* q, const void* k, const void* v, const void* out,
-                        const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t st) {
-    const BwdLayout lay = bwd_layout(pr);
+                        const void* dout, void* dq, void* dk, void* dv, void* ws, hipStream_t st,
+                        const void* y_saved = nullptr, const float* lse_saved = nullptr) {
+    const bool saved = y_saved != nullptr;
+    const BwdLayout lay = bwd_layout(pr, saved);
     char* w = static_cast<char*>(ws);
-    void *y = w + lay.y, *dy = w + lay.dy;
+    void* dy = w + lay.dy;
     void *gq = w + lay.gq, *gk = w + lay.gk;
     const bool bf16 = pr.dtype == SQUAD_BF16;
-    float* lse = bf16 ? reinterpret_cast<float*>(w + lay.lse) : nullptr;
     float* dl = bf16 ? reinterpret_cast<float*>(w + lay.dl) : nullptr;
-    // the forward keeps only O: recompute the local output Y (and, in bf16,
-    // its rows' log-sum-exp, which the local pass's backward then reuses)
-    const PassGeom gy = make_geom(pr, false);
-    hipError_t e = bf16 ? launch_pass_bf16(gy, pr.d, q, k, v, y, nullptr, lse, st)
-                        : launch_pass_f32(gy, pr.d, q, k, v, y, nullptr, st);
-    if (e != hipSuccess) return e;
+    const void* y = y_saved;
+    const float* lse = lse_saved;
+    hipError_t e = hipSuccess;
+    if (!saved) {
+        // the forward kept only O: recompute the local output Y (and, in
+        // bf16, its rows' log-sum-exp, which the local pass's backward reuses)
+        float* lse_w = bf16 ? reinterpret_cast<float*>(w + lay.lse) : nullptr;
+        e = run_local_saving(pr, q, k, v, w + lay.y, lse_w, st);
+        if (e != hipSuccess) return e;
+        y = w + lay.y;
+        lse = lse_w;
+    }
     // global pass (values Y, output O): its dQ, dK contributions, dY and, in
     // bf16, the local pass's D = rowsum(dY * Y)
     const PassGeom gg = make_geom(pr, true);
@@ -525,7 +597,44 @@ long long squad_attn_bwd_workspace_bytes(int B, int heads, int T, int Hs, int Ws
     if (squad::check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1;
     if (empty) return 0;
     pr.dtype = dtype;
-    return (long long)squad::bwd_layout(pr).total;
+    return (long long)squad::bwd_layout(pr, false).total;
+}
+
+long long squad_attn_bwd_saved_workspace_bytes(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww,
+                                               int d, int dtype) {
+    squad::Problem pr;
+    bool empty = false;
+    if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return -1;
+    if (squad::check_shape(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1;
+    if (empty) return 0;
+    pr.dtype = dtype;
+    return (long long)squad::bwd_layout(pr, true).total;
+}
+
+squad_status_t squad_attn_fwd_save(const void* q, const void* k, const void* v, void* out, void* y, float* lse,
+                                   int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype,
+                                   hipStream_t stream) {
+    squad::Problem pr;
+    bool empty = false;
+    const squad_status_t s =
+        squad::validate_save(q, k, v, out, y, lse, B, heads, T, Hs, Ws, wt, wh, ww, d, dtype, &pr, &empty);
+    if (s != SQUAD_OK || empty) return s;
+    hipError_t e = squad::run_local_saving(pr, q, k, v, y, dtype == SQUAD_BF16 ? lse : nullptr, stream);
+    if (e == hipSuccess) e = squad::run_pass(pr, true, q, k, y, out, nullptr, stream);
+    return squad::hip_status(e);
+}
+
+squad_status_t squad_attn_bwd_saved(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                    const void* y, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                                    size_t workspace_bytes, int B, int heads, int T, int Hs, int Ws, int wt, int wh,
+                                    int ww, int d, int dtype, hipStream_t stream) {
+    squad::Problem pr;
+    bool empty = false;
+    const squad_status_t s = squad::validate_bwd(q, k, v, out, dout, dq, dk, dv, workspace, workspace_bytes, B,
+                                                 heads, T, Hs, Ws, wt, wh, ww, d, dtype, &pr, &empty, true, y, lse);
+    if (s != SQUAD_OK || empty) return s;
+    return squad::hip_status(squad::run_backward(pr, q, k, v, out, dout, dq, dk, dv, workspace, stream, y,
+                                                 dtype == SQUAD_BF16 ? lse : nullptr));
 }
 
 double squad_attn_bwd_flops(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d) {
@@ -593,6 +702,6 @@ const char* squad_status_str(int status) {
 
 int squad_attn_last_hip_error(void) { return squad::g_last_hip_error; }
 
-int squad_attn_abi_version(void) { return 2; }
+int squad_attn_abi_version(void) { return 3; }
 
 }  // extern "C"

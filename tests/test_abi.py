@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(bd.ALL_SYMBOLS) == set(names)
     for n in names:
         assert getattr(lib, n) is not None
-    assert lib.squad_attn_abi_version() == 2
+    assert lib.squad_attn_abi_version() == 3
 
 
 def test_exports_via_nm():
@@ -277,7 +277,8 @@ def test_window_solver_matches_oracle_rule():
 
 DO, DQ, DK, DV = A + 16 * BYTES, A + 20 * BYTES, A + 24 * BYTES, A + 28 * BYTES
 BWS = A + 32 * BYTES
-# Y and dY in bf16, float32 dq and dk partials, float32 row log-sum-exp (256-byte rounded: exact here)
+# Y, dY and the global pass's dq, dk contributions in bf16, then float32 row log-sum-exp and D
+# (256-byte rounded: exact here)
 BWS_BYTES = 4 * BYTES + 2 * 18480 * 24 * 4
 
 
@@ -331,3 +332,71 @@ def test_bwd_check_accepts_what_would_launch():
                  dout=A + 8 * BYTES, dq=A + 10 * BYTES, dk=A + 12 * BYTES, dv=A + 14 * BYTES,
                  ws=A + 16 * BYTES, ws_bytes=8 * BYTES) == bd.SQUAD_OK
     assert bcall("bwd", B=0, q=0, k=0, v=0, out=0, dout=0, dq=0, dk=0, dv=0, ws=0) == bd.SQUAD_OK
+
+
+# ---------------------------------------------------------------------------
+# saved activations: squad_attn_fwd_save / squad_attn_bwd_saved (rejections only: a valid call would launch)
+
+Y, LSE = A + 40 * BYTES, A + 44 * BYTES
+SWS = A + 48 * BYTES
+LSE_BYTES = 18480 * 24 * 4
+SWS_BYTES = 3 * BYTES + LSE_BYTES  # dY and the dq, dk contributions in bf16, float32 row D
+
+
+def fcall(q=Q, k=K, v=V, out=O, y=Y, lse=LSE, dtype=bd.SQUAD_BF16, **over):
+    g = dict(GEO)
+    g.update(over)
+    return bd.lib().squad_attn_fwd_save(q, k, v, out, y, lse, g["B"], g["heads"], g["T"], g["Hs"], g["Ws"],
+                                        g["wt"], g["wh"], g["ww"], g["d"], dtype, None)
+
+
+def scall(q=Q, k=K, v=V, out=O, dout=DO, y=Y, lse=LSE, dq=DQ, dk=DK, dv=DV, ws=SWS, ws_bytes=SWS_BYTES,
+          dtype=bd.SQUAD_BF16, **over):
+    g = dict(GEO)
+    g.update(over)
+    return bd.lib().squad_attn_bwd_saved(q, k, v, out, dout, y, lse, dq, dk, dv, ws, ws_bytes, g["B"], g["heads"],
+                                         g["T"], g["Hs"], g["Ws"], g["wt"], g["wh"], g["ww"], g["d"], dtype, None)
+
+
+def test_saved_workspace_size():
+    assert bd.squad_attn_bwd_saved_workspace_bytes(*GEO.values(), bd.SQUAD_BF16) == SWS_BYTES
+    assert bd.squad_attn_bwd_saved_workspace_bytes(*GEO.values(), bd.SQUAD_F32) == 3 * 2 * BYTES
+    assert bd.squad_attn_bwd_saved_workspace_bytes(*dict(GEO, wh=3).values(), bd.SQUAD_BF16) == -1
+    assert bd.squad_attn_bwd_saved_workspace_bytes(*dict(GEO, B=0).values(), bd.SQUAD_BF16) == 0
+    assert bd.squad_attn_bwd_saved_workspace_bytes(*GEO.values(), 7) == -1
+    # the saved variant needs the recomputing one's workspace less Y and the log-sum-exp
+    assert BWS_BYTES - SWS_BYTES == BYTES + LSE_BYTES
+
+
+def test_fwd_save_rejections():
+    assert fcall(wh=3) == bd.SQUAD_ERR_SHAPE
+    assert fcall(d=96) == bd.SQUAD_ERR_UNSUPPORTED
+    assert fcall(q=0) == bd.SQUAD_ERR_NULL
+    assert fcall(y=0) == bd.SQUAD_ERR_NULL
+    assert fcall(lse=0) == bd.SQUAD_ERR_NULL                      # bf16 needs the log-sum-exp
+    assert fcall(y=Y + 8) == bd.SQUAD_ERR_ALIGN
+    assert fcall(lse=LSE + 4) == bd.SQUAD_ERR_ALIGN
+    assert fcall(y=O) == bd.SQUAD_ERR_ALIAS                       # y is not the output
+    assert fcall(y=V + 16) == bd.SQUAD_ERR_ALIAS
+    assert fcall(y=Q - BYTES + 16) == bd.SQUAD_ERR_ALIAS          # tail over q
+    assert fcall(lse=K + 64) == bd.SQUAD_ERR_ALIAS
+    assert fcall(lse=Y + BYTES - 16) == bd.SQUAD_ERR_ALIAS        # over y's tail
+    assert fcall(out=Q) == bd.SQUAD_ERR_ALIAS                     # the forward's own rule first
+
+
+def test_bwd_saved_rejections():
+    assert scall(wh=3) == bd.SQUAD_ERR_SHAPE
+    for key in ("q", "dout", "dv", "y", "lse"):
+        assert scall(**{key: 0}) == bd.SQUAD_ERR_NULL, key
+    assert scall(y=Y + 8) == bd.SQUAD_ERR_ALIGN
+    assert scall(lse=LSE + 4) == bd.SQUAD_ERR_ALIGN
+    assert scall(y=DQ) == bd.SQUAD_ERR_ALIAS                      # y over a gradient
+    assert scall(lse=DV + 64) == bd.SQUAD_ERR_ALIAS
+    assert scall(lse=Y + 16) == bd.SQUAD_ERR_ALIAS
+    assert scall(ws=0) == bd.SQUAD_ERR_WORKSPACE
+    assert scall(ws_bytes=SWS_BYTES - 1) == bd.SQUAD_ERR_WORKSPACE
+    assert scall(y=SWS + 256) == bd.SQUAD_ERR_ALIAS               # y inside the workspace
+    assert scall(lse=SWS + SWS_BYTES - 16) == bd.SQUAD_ERR_ALIAS
+    assert scall(dq=Q) == bd.SQUAD_ERR_ALIAS                      # the backward's own rules still hold
+    # float32 ignores lse (here odd): the call gets as far as the workspace, too small for float32
+    assert scall(dtype=bd.SQUAD_F32, lse=3) == bd.SQUAD_ERR_WORKSPACE

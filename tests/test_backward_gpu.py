@@ -132,3 +132,79 @@ def test_backward_long_windows_sampled_heads():
         check_grads([to_f64(t[0, :, h, :]) for t in (dq, dk, dv)], ref, "bf16", f"wan5b_4x h={h}")
     del qd, kd, vd, dod, out, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+# ---- saved activations: squad_attn_fwd_save + squad_attn_bwd_saved ----------
+# The pair runs the same kernels as squad_attn_fwd and squad_attn_bwd minus the
+# backward's recomputation of the local pass, so its results must be those of
+# the recomputing pair bit for bit (which the oracle checks above); the saved
+# Y must be the local pass alone, and the saved log-sum-exp that of each row's
+# window scores (log2 units of q.k * log2(e) / sqrt(d)).
+
+def run_saved(geo, dtype, B=1, heads=2, d=64, seed=0):
+    import torch
+    T, Hs, Ws, wt, wh, ww = geo
+    grid, window = (T, Hs, Ws), (wt, wh, ww)
+    n = T * Hs * Ws
+    log(f"case saved dtype={dtype} B={B} heads={heads} d={d} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww}")
+    q, k, v = wl.random_geometry_inputs(B, heads, n, d, dtype, seed=seed)
+    do = wl.random_geometry_inputs(B, heads, n, d, dtype, seed=seed + 1000)[0]
+    qd, kd, vd, dod = host_to_device((q, k, v, do), dtype)
+    out_ref = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    y_ref = bd.squad_attn_local(qd, kd, vd, grid, window)
+    out, y, lse = bd.squad_attn_fwd_save(qd, kd, vd, grid, window)
+    ref = bd.squad_attn_bwd(qd, kd, vd, out_ref, dod, grid, window)
+    got = bd.squad_attn_bwd_saved(qd, kd, vd, out, dod, y, lse, grid, window)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref)
+    assert torch.equal(y, y_ref)
+    assert all(torch.equal(a, b) for a, b in zip(got, ref))
+    if dtype == "bf16":
+        # every row's log-sum-exp from its window's scores, float64 on the bf16 inputs; the
+        # kernel sums the probabilities as rounded to bf16 for its P V product (unit roundoff
+        # 2^-8 each), so its log2 of the sum is exact to 2^-8 * log2(e) ~ 5.6e-3
+        qf, kf = to_f64(qd), to_f64(kd)
+        table = so.window_slot_table(*grid, *window)
+        lse_h = to_f64(lse)
+        c = np.log2(np.e) / np.sqrt(d)
+        for b in range(B):
+            for h in range(heads):
+                for rows in table:
+                    s = qf[b, rows, h, :] @ kf[b, rows, h, :].T * c
+                    mx = s.max(axis=1, keepdims=True)
+                    want = mx[:, 0] + np.log2(np.exp2(s - mx).sum(axis=1))
+                    np.testing.assert_allclose(lse_h[b, rows, h], want, rtol=0, atol=6e-3)
+    return q, k, v, do, got
+
+
+@pytest.mark.parametrize("geo", [GEOS[0], GEOS[3], GEOS[4]])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_saved_activations_match_recompute(geo, dtype):
+    T, Hs, Ws, wt, wh, ww = geo
+    q, k, v, do, got = run_saved(geo, dtype)
+    ref = so.squad_backward(q, k, v, do, (1, 2, T, Hs, Ws, wt, wh, ww, 64))
+    check_grads([to_f64(t) for t in got], ref, dtype, f"saved {geo}")
+
+
+def test_saved_activations_headline():
+    import torch
+    w = wl.WORKLOADS["wan5b_704p"]
+    log("case saved workload=wan5b_704p (generating inputs)")
+    qd, kd, vd = wl.device_inputs(w, seed=0)
+    dod = wl.device_inputs(w, seed=1)[0]
+    grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)
+    out_ref = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    out, y, lse = bd.squad_attn_fwd_save(qd, kd, vd, grid, window)
+    assert torch.equal(out, out_ref)
+    del out_ref
+    ref = bd.squad_attn_bwd(qd, kd, vd, out, dod, grid, window)
+    got = bd.squad_attn_bwd_saved(qd, kd, vd, out, dod, y, lse, grid, window)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(got, ref))
+    del ref
+    table = so.window_slot_table(*grid, *window)
+    q, k, v = wl.head_slices_f64(w, 0, 11)
+    ref11 = so.squad_backward_head(q, k, v, to_f64(dod[0, :, 11, :]), table)
+    check_grads([to_f64(t[0, :, 11, :]) for t in got], ref11, "bf16", "saved wan5b_704p h=11")
+    del qd, kd, vd, dod, out, y, lse, got
+    torch.cuda.empty_cache()
