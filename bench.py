@@ -461,7 +461,25 @@ def main():
                        "kernel_bytes": bwd_bytes, "gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
                        "mfma_peak_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                        "hbm_peak_frac": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    del dq, dk, dv, dout, ws
+    # ---- the same gradients from saved activations (squad_attn_fwd_save's Y
+    # and log-sum-exp, made untimed per input set): no recomputation ---------
+    del ws
+    ws = torch.empty(bd.squad_attn_bwd_saved_workspace_bytes(*w.geometry(), dt), dtype=torch.uint8, device="cuda")
+    saved = [bd.squad_attn_fwd_save(s[0], s[1], s[2], grid, window, out=s[3])[1:] for s in sets]
+    which = {id(s): i for i, s in enumerate(sets)}
+
+    def bwd_saved(s):
+        y, lse = saved[which[id(s)]]
+        bd.squad_attn_bwd_saved(s[0], s[1], s[2], s[3], dout, y, lse, grid, window, dq=dq, dk=dk, dv=dv,
+                                workspace=ws)
+
+    sv_ms = time_loop(bwd_saved, max(args.kernel_iters // 5, 5), sets)
+    sv_bytes = bwd_bytes - 4.0 * w.B * w.n * w.heads * w.d * (2 if dt == bd.SQUAD_BF16 else 4)
+    eprint(f"[bench] backward from saved activations {sv_ms:.4f} ms "
+           f"({bwd_flops / (sv_ms * 1e-3) / 1e12:.1f} TFLOP/s)")
+    out["backward_saved"] = {"ms": sv_ms, "tflops": bwd_flops / (sv_ms * 1e-3) / 1e12, "kernel_bytes": sv_bytes,
+                             "gbs": sv_bytes / (sv_ms * 1e-3) / 1e9}
+    del dq, dk, dv, dout, ws, saved
 
     if args.copy_calibration_mib > 0:
         nbytes = args.copy_calibration_mib << 20
