@@ -592,15 +592,16 @@ int grid_for(const void* kern, int threads, int nprob, int mult) {
 // the waves of one workgroup; a workgroup has at least NCH/64 waves (8 at
 // d = 128, 4 at d = 64) so that every thread stages one chunk per tensor.  The
 // register budget follows the waves that share a SIMD (<= 12 waves: 168
-// VGPRs; 8 waves: 256).  Problems of up to 12 tiles run one tile per wave.
-// Longer ones are split into 2 or 3 parts of query rows (items) run by that
-// same instance when the problem count is a multiple of 8 and the pass is
-// not in place (a part writes its rows of `out` while another part of the
-// problem may still be reading them as values otherwise): the parts of a
-// problem are 8 items apart and the grid is a multiple of 8 * parts, so they
-// run in the same round on workgroups 8 apart, which round-robin dispatch puts
-// on the same XCD, and their repeated key / value reads are served by its L2.
-// Otherwise 2, 3 or 4 tiles go on each wave.  The unpadded local pass takes
+// VGPRs; 8 waves: 256).  Problems of up to 12 tiles run one tile per wave, of
+// 13-24 tiles 2 or 3 tiles per wave on 8 waves (each key and value read once).
+// Longer ones are split into 3 parts of query rows (items) run by the 1-tile
+// instance when the problem count is a multiple of 8 and the pass is not in
+// place (a part writes its rows of `out` while another part of the problem
+// may still be reading them as values otherwise): the parts of a problem are
+// 8 items apart and the grid is a multiple of 8 * parts, so they run in the
+// same round on workgroups 8 apart, which round-robin dispatch puts on the
+// same XCD, and their repeated key / value reads are mostly served by its L2.
+// Otherwise 4 tiles go on each wave (whose registers spill).  The unpadded local pass takes
 // the FAST loader when a batch element of a tensor spans less than 4 GiB.
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool FAST, bool SPLIT = false>
 hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o, void* y,
@@ -632,7 +633,7 @@ hipError_t launch_menu(const PassGeom& g0, const void* q, const void* k, const v
     constexpr int minw = Geo<D>::NCH / 64;
     const int tiles = (g0.L + 15) / 16;
     PassGeom g = g0;
-    if (tiles > 12 && g.nprob % 8 == 0 && v != o) {
+    if (tiles > 24 && g.nprob % 8 == 0 && v != o) {
         g.parts = (tiles + 11) / 12;
         g.part_tiles = (tiles + g.parts - 1) / g.parts;
         g.nitems = g.nprob * g.parts;

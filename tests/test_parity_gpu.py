@@ -246,12 +246,13 @@ def test_many_heads_small_dim(dtype, op):
 
 
 # ---------------------------------------------------------------------------
-# Long problems split into query parts (problem count a multiple of 8)
+# Long problems: whole on the 2- and 3-tile instances up to 24 tiles, split
+# into query parts beyond (problem count a multiple of 8, not in place)
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("geo,heads", [
-    ((21, 8, 8, 21, 4, 4), 8),     # m = 336: 2 parts of 11 + 10 tiles, 32 local problems
-    ((5, 10, 16, 5, 5, 8), 2),     # m = 200: 7 + 6 tiles, ragged last block
+    ((21, 8, 8, 21, 4, 4), 8),     # m = 336: 21 tiles on the 3-tile instance, 32 local problems
+    ((5, 10, 16, 5, 5, 8), 2),     # m = 200: 13 tiles on the 2-tile instance, ragged last block
     ((5, 16, 10, 5, 8, 10), 4),    # m = 400: 3 parts of 9 + 9 + 7 tiles
     ((8, 8, 16, 8, 8, 8), 4),      # m = 512: 3 parts of 11 + 11 + 10 tiles
 ])
@@ -261,11 +262,13 @@ def test_split_long_problems(geo, heads, op):
 
 
 def test_split_long_problems_head_dim_64():
-    run_small((21, 8, 8, 21, 4, 4), "bf16", "local", heads=8, d=64, seed=18)
+    run_small((21, 8, 8, 21, 4, 4), "bf16", "local", heads=8, d=64, seed=18)   # whole, 3 tiles per wave
+    run_small((5, 16, 10, 5, 8, 10), "bf16", "local", heads=4, d=64, seed=18)  # 3 parts
 
 
 def test_split_many_slots_global():
-    # global pass over N_w = 200 windows at each of 8 slots x 2 heads (16 problems)
+    # global pass over N_w = 200 windows at each of 8 slots x 2 heads (16 problems,
+    # 13 tiles: whole on the 2-tile instance)
     run_small((2, 20, 80, 1, 2, 4), "bf16", "global", heads=2, d=64, seed=19)
 
 
