@@ -8,8 +8,8 @@
 //
 // Workgroup organisation
 //   * Persistent: a workgroup walks work items blockIdx.x, +gridDim.x, ...: a
-//     whole problem, or (long problems of a pass that is not in place) one of
-//     the 2-3 parts of its query rows.  A whole problem is owned by one
+//     whole problem, or (problems of more than 24 query tiles, in a pass that
+//     is not in place) one of the 2 parts of its query rows.  A whole problem is owned by one
 //     workgroup, which reads all of its rows before it writes any (this is
 //     what makes the in-place global pass safe).
 //   * The work of an item is NB = ceil(L/32) steps.  Step b brings in 32 rows
@@ -32,8 +32,8 @@
 //     refreshed running maximum (refreshed only when a block's maximum exceeds
 //     it by more than 2^8), so the accumulator rescale is rare and P <= 256;
 //     the cross-lane reduction of the block maximum runs only then.
-//     On request (the backward's recompute of the local output) each row's
-//     log-sum-exp is stored as well.
+//     On request (the training forward's local pass, and the backward's
+//     recompute of it) each row's log-sum-exp is stored as well.
 #include "squad_internal.h"
 #include "squad_layout.h"
 #include "squad_mfma.h"
@@ -594,7 +594,7 @@ int grid_for(const void* kern, int threads, int nprob, int mult) {
 // register budget follows the waves that share a SIMD (<= 12 waves: 168
 // VGPRs; 8 waves: 256).  Problems of up to 12 tiles run one tile per wave, of
 // 13-24 tiles 2 or 3 tiles per wave on 8 waves (each key and value read once).
-// Longer ones are split into 3 parts of query rows (items) run by the 1-tile
+// Longer ones are split into 2 parts of query rows (items) run by the 2-tile
 // instance when the problem count is a multiple of 8 and the pass is not in
 // place (a part writes its rows of `out` while another part of the problem
 // may still be reading them as values otherwise): the parts of a problem are
@@ -634,13 +634,13 @@ hipError_t launch_menu(const PassGeom& g0, const void* q, const void* k, const v
     const int tiles = (g0.L + 15) / 16;
     PassGeom g = g0;
     if (tiles > 24 && g.nprob % 8 == 0 && v != o) {
-        g.parts = (tiles + 11) / 12;
+        g.parts = (tiles + 15) / 16;
         g.part_tiles = (tiles + g.parts - 1) / g.parts;
         g.nitems = g.nprob * g.parts;
         g.div_parts = make_fastdiv((uint32_t)g.parts);
     }
     const int waves = g.part_tiles > minw ? g.part_tiles : minw;
-    if (g.parts > 1) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, FAST, true>(g, waves, q, k, v, o, y, lse, st);
+    if (g.parts > 1) return launch_one<D, 2, 8, 4, 2, 256, true, PAD, FAST, true>(g, 8, q, k, v, o, y, lse, st);
     if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, FAST>(g, waves, q, k, v, o, y, lse, st);
     if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
     if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);

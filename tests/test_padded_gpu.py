@@ -129,5 +129,5 @@ def test_solved_windows_run():
 def test_padded_split_long_windows():
     # m = 315 with 4 heads: 440 local problems of 20 tiles, whole on the 3-tile instance
     run_padded((21, 30, 52, 21, 3, 5), "bf16", heads=4, d=128, seed=11)
-    # m = 400 with 8 heads: 24 local problems of 25 tiles (grid padded to 5x24x10), three query parts
+    # m = 400 with 8 heads: 24 local problems of 25 tiles (grid padded to 5x24x10), two query parts
     run_padded((5, 17, 10, 5, 8, 10), "bf16", heads=8, d=128, seed=12)
