@@ -124,9 +124,13 @@ squad_status_t squad_attn_fwd_reversed(const void* q, const void* k, const void*
  * q, k, v, out: [B, n, heads, d] as for squad_attn_fwd (n = T*Hs*Ws, the real
  * grid).  workspace: device buffer of at least
  * squad_attn_padded_workspace_bytes(...) bytes, 16-byte aligned, holding the
- * local outputs of the padded positions between the two passes (contents on
- * entry ignored, undefined afterwards; must not overlap q, k, v or out; one
- * workspace must not be used by two calls that may run at the same time).
+ * local outputs of the padded positions between the two passes and, in bf16
+ * when the global pass has more than 384 windows and B*heads*m is a multiple
+ * of 8, the local outputs of the real tokens too (the global pass then reads
+ * its values there instead of from `out`, which lets it split its long
+ * problems into query parts) (contents on entry ignored, undefined
+ * afterwards; must not overlap q, k, v or out; one workspace must not be used
+ * by two calls that may run at the same time).
  * When the window tiles the grid the call is squad_attn_fwd: the workspace is
  * not used (it may be NULL) and out may be v.  Otherwise out must not overlap
  * v either (mirror images read other windows' rows of v).
@@ -149,9 +153,10 @@ squad_status_t squad_attn_check_padded(const void* q, const void* k, const void*
                                        int wt, int wh, int ww, int d, int dtype);
 
 /* Bytes of workspace squad_attn_fwd_padded needs: B * (padded positions per
- * batch element) * heads * d * sizeof(dtype); 0 when the window tiles the grid
- * or the problem is empty; -1 on a shape or dtype the padded entry point
- * rejects.  Pure host function. */
+ * batch element) * heads * d * sizeof(dtype), plus, in the case above, that
+ * rounded up to 256 bytes and B * n * heads * d * sizeof(dtype) after it; 0
+ * when the window tiles the grid or the problem is empty; -1 on a shape or
+ * dtype the padded entry point rejects.  Pure host function. */
 long long squad_attn_padded_workspace_bytes(int B, int heads, int T, int Hs, int Ws,
                                             int wt, int wh, int ww, int d, int dtype);
 

@@ -26,7 +26,9 @@ struct Problem {
     // then counts the windows of the padded grid
     int Hp = 0, Wp = 0;
     int64_t np = 0, npad = 0;
-    size_t ws_bytes = 0;  // B*npad*heads*d*sizeof(dtype)
+    // the padded entry point's workspace: the side buffer (B*npad*heads*d in
+    // the dtype) and, at ybuf_off when that is not 0, Y of the real tokens
+    size_t ws_bytes = 0, ybuf_off = 0;
 };
 
 int esize(int dtype) { return dtype == SQUAD_BF16 ? 2 : 4; }
@@ -140,6 +142,24 @@ squad_status_t validate(const void* q, const void* k, const void* v, const void*
     return SQUAD_OK;
 }
 
+PassGeom make_geom(const Problem& pr, bool global);
+
+// The padded entry point's workspace (pr shaped by check_shape_padded, dtype
+// set): the side buffer, and, when the grid is padded and the bf16 global pass
+// would split its problems were it not in place, Y of every real token after
+// it, so that the local pass writes Y there and the global pass reads its
+// values from there and writes `out` (not in place).
+void padded_workspace(Problem* pr) {
+    const size_t es = (size_t)esize(pr->dtype);
+    const size_t side = (size_t)pr->B * (size_t)pr->npad * (size_t)pr->heads * (size_t)pr->d * es;
+    pr->ybuf_off = 0;
+    pr->ws_bytes = side;
+    if (pr->npad > 0 && pr->dtype == SQUAD_BF16 && pass_bf16_splits(make_geom(*pr, true))) {
+        pr->ybuf_off = (side + 255) & ~(size_t)255;
+        pr->ws_bytes = pr->ybuf_off + (size_t)pr->B * (size_t)pr->n * (size_t)pr->heads * (size_t)pr->d * es;
+    }
+}
+
 // Arguments of the padded entry points: the checks of validate() in the same
 // order, plus the side buffer (SQUAD_ERR_WORKSPACE after the NULL checks).
 // When the window tiles the grid nothing is padded, the workspace is ignored
@@ -159,7 +179,7 @@ squad_status_t validate_padded(const void* q, const void* k, const void* v, cons
     if (padded && (T > kMaxPaddedT || pr->Hp > kMaxPaddedHW || pr->Wp > kMaxPaddedHW)) return SQUAD_ERR_UNSUPPORTED;
     pr->dtype = dtype;
     if (!q || !k || !v || !out) return SQUAD_ERR_NULL;
-    pr->ws_bytes = (size_t)pr->B * (size_t)pr->npad * (size_t)pr->heads * (size_t)d * (size_t)esize(dtype);
+    padded_workspace(pr);
     if (padded && (!ws || ws_size < pr->ws_bytes)) return SQUAD_ERR_WORKSPACE;
     uintptr_t bits = ((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)out);
     if (padded) bits |= (uintptr_t)ws;
@@ -516,6 +536,12 @@ squad_status_t squad_attn_fwd_padded(const void* q, const void* k, const void* v
     const squad_status_t s = squad::validate_padded(q, k, v, out, workspace, workspace_bytes, B, heads, T, Hs, Ws,
                                                     wt, wh, ww, d, dtype, &pr, &empty);
     if (s != SQUAD_OK || empty) return s;
+    if (pr.ybuf_off > 0) {
+        void* ybuf = static_cast<char*>(workspace) + pr.ybuf_off;
+        hipError_t e = squad::run_pass(pr, false, q, k, v, ybuf, workspace, stream);
+        if (e == hipSuccess) e = squad::run_pass(pr, true, q, k, ybuf, out, workspace, stream);
+        return squad::hip_status(e);
+    }
     return squad::hip_status(
         squad::run_two_passes(pr, true, q, k, v, out, pr.npad > 0 ? workspace : nullptr, stream));
 }
@@ -536,9 +562,11 @@ long long squad_attn_padded_workspace_bytes(int B, int heads, int T, int Hs, int
     if (dtype != SQUAD_BF16 && dtype != SQUAD_F32) return -1;
     if (squad::check_shape_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, &pr, &empty) != SQUAD_OK) return -1;
     if (empty) return 0;
-    const long double bytes = (long double)B * pr.npad * heads * d * squad::esize(dtype);
+    const long double bytes = (long double)B * (pr.npad + pr.n) * heads * d * squad::esize(dtype) + 256;
     if (bytes >= 9.0e18L) return -1;
-    return (long long)bytes;
+    pr.dtype = dtype;
+    squad::padded_workspace(&pr);
+    return (long long)pr.ws_bytes;
 }
 
 double squad_attn_flops_padded(int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww, int d) {

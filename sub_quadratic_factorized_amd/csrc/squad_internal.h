@@ -171,6 +171,10 @@ hipError_t launch_pass_bf16(const PassGeom& g, int d, const void* q, const void*
 hipError_t launch_pass_f32(const PassGeom& g, int d, const void* q, const void* k,
                            const void* vals, void* out, void* ypad, hipStream_t stream);
 
+// Whether launch_pass_bf16 splits the problems of g into query parts when the
+// pass is not in place (vals != out); in place it never does.
+bool pass_bf16_splits(const PassGeom& g);
+
 // Operands of one pass's backward (unpadded grids).  q, k, vals: the pass's
 // inputs; out: its output O; dout: the upstream gradient dO.  The kernels
 // write dQ and dK (plus addq / addk when those are not null: the other pass's

@@ -627,13 +627,19 @@ hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k
     return hipGetLastError();
 }
 
+// Problems of more query tiles than this are split into query parts when the
+// pass is not in place and the problem count is a multiple of 8.
+constexpr int kSplitTiles = 24;
+
+bool splits(const PassGeom& g) { return (g.L + 15) / 16 > kSplitTiles && g.nprob % 8 == 0; }
+
 template <int D, bool PAD, bool FAST>
 hipError_t launch_menu(const PassGeom& g0, const void* q, const void* k, const void* v, void* o, void* y, float* lse,
                        hipStream_t st) {
     constexpr int minw = Geo<D>::NCH / 64;
     const int tiles = (g0.L + 15) / 16;
     PassGeom g = g0;
-    if (tiles > 24 && g.nprob % 8 == 0 && v != o) {
+    if (splits(g) && v != o) {
         g.parts = (tiles + 15) / 16;
         g.part_tiles = (tiles + g.parts - 1) / g.parts;
         g.nitems = g.nprob * g.parts;
@@ -656,6 +662,8 @@ hipError_t launch_d(const PassGeom& g, const void* q, const void* k, const void*
 }
 
 }  // namespace
+
+bool pass_bf16_splits(const PassGeom& g) { return splits(g); }
 
 hipError_t launch_pass_bf16(const PassGeom& g, int d, const void* q, const void* k, const void* vals, void* out,
                             void* ypad, float* lse_out, hipStream_t stream) {

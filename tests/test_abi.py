@@ -400,3 +400,17 @@ def test_bwd_saved_rejections():
     assert scall(dq=Q) == bd.SQUAD_ERR_ALIAS                      # the backward's own rules still hold
     # float32 ignores lse (here odd): the call gets as far as the workspace, too small for float32
     assert scall(dtype=bd.SQUAD_F32, lse=3) == bd.SQUAD_ERR_WORKSPACE
+
+
+def test_padded_workspace_holds_y_for_long_global_passes():
+    # grid 1x21x79 padded to 1x21x80, window 1x1x4: 420 windows (27 query tiles) in the global pass,
+    # 21 padded tokens; with B*heads*m a multiple of 8 the bf16 workspace also holds Y of the 1659
+    # real tokens, after the side buffer rounded up to 256 bytes
+    side = 1 * 21 * 2 * 64 * 2
+    assert bd.squad_attn_padded_workspace_bytes(1, 2, 1, 21, 79, 1, 1, 4, 64, bd.SQUAD_BF16) == \
+        (side + 255) // 256 * 256 + 1659 * 2 * 64 * 2
+    assert bd.squad_attn_padded_workspace_bytes(1, 2, 1, 21, 79, 1, 1, 4, 64, bd.SQUAD_F32) == 2 * side
+    # B*heads*m = 4: the global pass could not split, so the side buffer alone
+    assert bd.squad_attn_padded_workspace_bytes(1, 1, 1, 21, 79, 1, 1, 4, 64, bd.SQUAD_BF16) == side // 2
+    # 384 windows (24 tiles) or fewer: the side buffer alone
+    assert bd.squad_attn_padded_workspace_bytes(1, 2, 1, 21, 71, 1, 1, 4, 64, bd.SQUAD_BF16) == 1 * 21 * 2 * 64 * 2

@@ -126,6 +126,14 @@ def test_solved_windows_run():
         run_padded(grid + win, "bf16", heads=2, d=128, seed=sum(grid))
 
 
+@pytest.mark.parametrize("stale", [False, True])
+def test_padded_long_global_pass_reads_y_from_workspace(stale):
+    # 420 windows at each of 4 slots (27 query tiles; B*heads*m = 8): the local pass writes Y into
+    # the workspace and the global pass reads it there, split into two query parts
+    run_padded((1, 21, 79, 1, 1, 4), "bf16", heads=2, d=64, seed=21, stale_workspace=stale)
+    run_padded((1, 21, 79, 1, 1, 4), "bf16", heads=2, d=128, seed=22)
+
+
 def test_padded_split_long_windows():
     # m = 315 with 4 heads: 440 local problems of 20 tiles, whole on the 3-tile instance
     run_padded((21, 30, 52, 21, 3, 5), "bf16", heads=4, d=128, seed=11)
