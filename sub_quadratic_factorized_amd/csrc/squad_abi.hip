@@ -284,7 +284,8 @@ BwdLayout bwd_layout(const Problem& pr, bool saved) {
 // dtype) and, in bf16, lse ([B, n, heads] float32).  Both non-NULL (lse in bf16
 // only), 16-byte aligned, and overlapping none of `tensors` (a forward's
 // output, or a backward's gradients) nor each other.
-squad_status_t check_saved(const Problem& pr, const void* y, const void* lse, const void* const* tensors, int ntensors) {
+squad_status_t check_saved(const Problem& pr, const void* y, const void* lse, const void* const* tensors,
+                           int ntensors) {
     const bool bf16 = pr.dtype == SQUAD_BF16;
     if (!y || (bf16 && !lse)) return SQUAD_ERR_NULL;
     if (((uintptr_t)y | (bf16 ? (uintptr_t)lse : 0)) & 15u) return SQUAD_ERR_ALIGN;
