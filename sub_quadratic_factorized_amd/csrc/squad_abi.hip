@@ -719,9 +719,10 @@ const char* squad_status_str(int status) {
     switch (status) {
         case SQUAD_OK: return "ok";
         case SQUAD_ERR_NULL: return "null pointer argument";
-        case SQUAD_ERR_SHAPE: return "invalid shape (non-positive extent, window not tiling the grid, or size overflow)";
+        case SQUAD_ERR_SHAPE:
+            return "invalid shape (non-positive extent, window not tiling the grid, or size overflow)";
         case SQUAD_ERR_UNSUPPORTED: return "unsupported dtype, head dim, or sequence length";
-        case SQUAD_ERR_ALIAS: return "output overlaps an input (only out == v is allowed)";
+        case SQUAD_ERR_ALIAS: return "a written buffer overlaps another buffer of the call (only out == v is allowed)";
         case SQUAD_ERR_ALIGN: return "pointer not 16-byte aligned";
         case SQUAD_ERR_HIP: return "HIP runtime or launch error";
         case SQUAD_ERR_WORKSPACE: return "workspace missing or smaller than squad_attn_padded_workspace_bytes";
