@@ -322,13 +322,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
             float pr0[4], pr1[4], ds0[4], ds1[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                // On 8 waves D is read for rows past L too (< NB * BR <= kMaxLen: unused
+                // LDS entries, dropped by the selects), which keeps the loop free of
+                // branches; on 12 waves, whose registers are tighter, only for live rows.
                 const int q0 = qb * BR + 4 * lg + i, q1 = q0 + 16;
+                float d0 = 0.0f, d1 = 0.0f;
+                if constexpr (NW <= 8) {
+                    d0 = dd[q0];
+                    d1 = dd[q1];
+                }
                 const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -lse[q0]));
                 const float e1 = __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -lse[q1]));
                 pr0[i] = q0 < L ? e0 : 0.0f;
                 pr1[i] = q1 < L ? e1 : 0.0f;
-                ds0[i] = q0 < L ? e0 * (pa[i] - dd[q0]) : 0.0f;
-                ds1[i] = q1 < L ? e1 * (pb[i] - dd[q1]) : 0.0f;
+                ds0[i] = q0 < L ? e0 * (pa[i] - (NW <= 8 ? d0 : dd[q0])) : 0.0f;
+                ds1[i] = q1 < L ? e1 * (pb[i] - (NW <= 8 ? d1 : dd[q1])) : 0.0f;
             }
             const bf16x8 pp = pack8(pr0, pr1), dsp = pack8(ds0, ds1);
 #pragma unroll
