@@ -88,6 +88,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
     const int base = g.global ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
     const int64_t bh = (int64_t)pr.b * g.n * row_stride + (int64_t)pr.h * D;
     for (int r = tid; r < L; r += blockDim.x) tab[r] = g.global ? win_origin(g, r) : slot_offset(g, r);
+    // rows past L up to the last block's end (NB * BR <= kMaxLen): log-sum-exp
+    // +inf and D 0, so that the key sweep's probabilities and dS of such query
+    // rows come out 0 without masking
+    for (int r = L + tid; r < NB * BR; r += blockDim.x) {
+        lse[r] = INFINITY;
+        dd[r] = 0.0f;
+    }
     __syncthreads();
     // element offset of row r of the problem (rows past the end clamped)
     auto row = [&](int r) -> int64_t { return bh + (int64_t)(base + tab[min(r, L - 1)]) * row_stride; };
@@ -241,14 +248,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                 pa = mfma(row_op(rowB[u & 1], 0, s), doreg[s], pa);  // dP^T
                 pb = mfma(row_op(rowB[u & 1], 1, s), doreg[s], pb);
             }
-            if (!HASLSE) {
-                float mx = -INFINITY;
+            // keys past L (the last block only): score -inf, probability exp2(-inf) = 0
+            if (blk == NB - 1) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (blk * BR + 4 * lg + i >= L) sa[i] = -INFINITY;
                     if (blk * BR + 16 + 4 * lg + i >= L) sb[i] = -INFINITY;
-                    mx = fmaxf(mx, fmaxf(sa[i], sb[i]));
                 }
+            }
+            if (!HASLSE) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(sa[i], sb[i]));
                 if (__builtin_amdgcn_ballot_w64(mx * c_log2 > m + kHeadroom) != 0) {
                     const float mnew = fmaxf(m, row_max4(mx) * c_log2);
                     const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -262,9 +273,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
             float ds0[4], ds1[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool v0 = blk * BR + 4 * lg + i < L, v1 = blk * BR + 16 + 4 * lg + i < L;
-                const float e0 = v0 ? __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -sub)) : 0.0f;
-                const float e1 = v1 ? __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -sub)) : 0.0f;
+                const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -sub));
+                const float e1 = __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -sub));
                 if (!HASLSE) lpart += e0 + e1;
                 ds0[i] = e0 * (pa[i] - Dq);
                 ds1[i] = e1 * (pb[i] - Dq);
@@ -322,21 +332,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
             float pr0[4], pr1[4], ds0[4], ds1[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // On 8 waves D is read for rows past L too (< NB * BR <= kMaxLen: unused
-                // LDS entries, dropped by the selects), which keeps the loop free of
-                // branches; on 12 waves, whose registers are tighter, only for live rows.
+                // query rows past L: lse +inf and D 0 (set at the start), so P = 0, dS = 0
                 const int q0 = qb * BR + 4 * lg + i, q1 = q0 + 16;
-                float d0 = 0.0f, d1 = 0.0f;
-                if constexpr (NW <= 8) {
-                    d0 = dd[q0];
-                    d1 = dd[q1];
-                }
                 const float e0 = __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -lse[q0]));
                 const float e1 = __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -lse[q1]));
-                pr0[i] = q0 < L ? e0 : 0.0f;
-                pr1[i] = q1 < L ? e1 : 0.0f;
-                ds0[i] = q0 < L ? e0 * (pa[i] - (NW <= 8 ? d0 : dd[q0])) : 0.0f;
-                ds1[i] = q1 < L ? e1 * (pb[i] - (NW <= 8 ? d1 : dd[q1])) : 0.0f;
+                pr0[i] = e0;
+                pr1[i] = e1;
+                ds0[i] = e0 * (pa[i] - dd[q0]);
+                ds1[i] = e1 * (pb[i] - dd[q1]);
             }
             const bf16x8 pp = pack8(pr0, pr1), dsp = pack8(ds0, ds1);
 #pragma unroll
