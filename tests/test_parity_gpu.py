@@ -220,6 +220,29 @@ def test_deterministic():
     assert torch.equal(a, b)
 
 
+def test_side_stream_matches_default_stream():
+    # the calls enqueue on the stream they are given (torch's current one by default): on a side
+    # stream, after waiting for the inputs, forward and backward give the default stream's bits
+    import torch
+    w = wl.WORKLOADS["wan5b_704p"]
+    grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)
+    qd, kd, vd = workload_device_inputs(w)
+    dod = wl.device_inputs(w, seed=1)[0]
+    ref = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    ref_g = bd.squad_attn_bwd(qd, kd, vd, ref, dod, grid, window)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        out = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+        grads = bd.squad_attn_bwd(qd, kd, vd, out, dod, grid, window)
+    out2 = torch.empty_like(qd)
+    bd.squad_attn_fwd(qd, kd, vd, grid, window, out=out2, stream=side.cuda_stream)
+    side.synchronize()
+    assert torch.equal(out, ref) and torch.equal(out2, ref)
+    assert all(torch.equal(a, b) for a, b in zip(grads, ref_g))
+
+
 def test_empty_batch_is_noop():
     import torch
     q = torch.empty((0, 48, 2, 64), device="cuda", dtype=torch.bfloat16)
