@@ -186,6 +186,15 @@ def test_saved_activations_match_recompute(geo, dtype):
     check_grads([to_f64(t) for t in got], ref, dtype, f"saved {geo}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_saved_activations_batch_head_dim_128(dtype):
+    geo = (3, 8, 10, 3, 2, 5)
+    T, Hs, Ws, wt, wh, ww = geo
+    q, k, v, do, got = run_saved(geo, dtype, B=2, heads=3, d=128, seed=7)
+    ref = so.squad_backward(q, k, v, do, (2, 3, T, Hs, Ws, wt, wh, ww, 128))
+    check_grads([to_f64(t) for t in got], ref, dtype, f"saved B=2 {geo}")
+
+
 def test_saved_activations_headline():
     import torch
     w = wl.WORKLOADS["wan5b_704p"]
