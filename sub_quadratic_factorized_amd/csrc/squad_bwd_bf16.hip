@@ -7,7 +7,7 @@
 //     dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),  dV = P^T dO.
 //
 // One workgroup of 8 or 12 waves per problem; rows stream through LDS in
-// blocks of 32 (clamped past the end, masked) along one sequence of steps: per
+// blocks of 32 (clamped past the end) along one sequence of steps: per
 // group of query tiles, NB steps over K and V; per group of key tiles, NB steps
 // over Q and dO.  Every thread stages one 16-byte chunk of each of the step's
 // two tensors in registers PD steps ahead of use, with unconditional loads,
@@ -23,15 +23,18 @@
 // Query sweep (waves own 16-query tiles): D from dO and O (or given per row:
 // then O is not read), then one pass over K and V accumulating dQ^T; when the
 // rows' log-sum-exp is given (HASLSE: the local pass, whose forward the
-// backward has just recomputed) P is formed from it, otherwise dQ^T
-// accumulates unnormalised probabilities under a running maximum and is
-// divided by the row sum at the end of the pass, which also yields the
-// log-sum-exp.  Key sweep (waves own 16-key tiles): a pass over Q and dO
-// accumulating dV^T and dK^T from P and dS recomputed with the stored
+// backward has recomputed or the training forward kept) P is formed from it,
+// otherwise dQ^T accumulates unnormalised probabilities under a running
+// maximum and is divided by the row sum at the end of the pass, which also
+// yields the log-sum-exp.  Key sweep (waves own 16-key tiles): a pass over Q
+// and dO accumulating dV^T and dK^T from P and dS recomputed with the stored
 // log-sum-exp and D, and optionally rowsum(dV * V) of the values rows (D of
 // the backward of the pass that produced the values, which then need not read
-// them again).  P and dS enter their MFMAs rounded to bf16, and the other
-// pass's contributions to dQ and dK arrive in bf16; all sums are float32.
+// them again).  Rows past the end cost no per-element masks: keys there get a
+// score of -inf in a problem's last block only, and query rows there a
+// log-sum-exp of +inf and a D of 0, so their P and dS come out 0.  P and dS
+// enter their MFMAs rounded to bf16, and the other pass's contributions to dQ
+// and dK arrive in bf16; all sums are float32.
 #include "squad_internal.h"
 #include "squad_layout.h"
 #include "squad_mfma.h"
