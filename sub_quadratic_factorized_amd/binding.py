@@ -401,3 +401,34 @@ def squad_attn_bwd_saved(q, k, v, out, dout, y, lse, grid, window, dq=None, dk=N
     if st != SQUAD_OK:
         raise SquadError(st, "squad_attn_bwd_saved")
     return dq, dk, dv
+
+
+_autograd_fn = None
+
+
+def squad_attention(q, k, v, grid, window):
+    """Differentiable squad_attn_fwd for torch autograd: the forward runs
+    squad_attn_fwd_save and keeps (q, k, v, out, Y, lse) for the backward,
+    which runs squad_attn_bwd_saved (windows must tile the grid)."""
+    global _autograd_fn
+    if _autograd_fn is None:
+        import torch
+
+        class SquadAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, grid, window):
+                out, y, lse = squad_attn_fwd_save(q, k, v, grid, window)
+                saved = (q, k, v, out, y) + ((lse,) if lse is not None else ())
+                ctx.save_for_backward(*saved)
+                ctx.grid, ctx.window = grid, window
+                return out
+
+            @staticmethod
+            def backward(ctx, dout):
+                q, k, v, out, y, *rest = ctx.saved_tensors
+                dq, dk, dv = squad_attn_bwd_saved(q, k, v, out, dout.contiguous(), y, rest[0] if rest else None,
+                                                  ctx.grid, ctx.window)
+                return dq, dk, dv, None, None
+
+        _autograd_fn = SquadAttention
+    return _autograd_fn.apply(q, k, v, tuple(grid), tuple(window))

@@ -217,3 +217,24 @@ def test_saved_activations_headline():
     check_grads([to_f64(t[0, :, 11, :]) for t in got], ref11, "bf16", "saved wan5b_704p h=11")
     del qd, kd, vd, dod, out, y, lse, got
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_autograd_wrapper_matches_entry_points(dtype):
+    # squad_attention through torch autograd: the saved-activation pair, so the same bits as
+    # squad_attn_fwd and squad_attn_bwd
+    import torch
+    geo = (4, 8, 12, 2, 4, 4)
+    T, Hs, Ws, wt, wh, ww = geo
+    grid, window = (T, Hs, Ws), (wt, wh, ww)
+    q, k, v = wl.random_geometry_inputs(1, 2, T * Hs * Ws, 64, dtype, seed=41)
+    do = wl.random_geometry_inputs(1, 2, T * Hs * Ws, 64, dtype, seed=42)[0]
+    qd, kd, vd, dod = host_to_device((q, k, v, do), dtype)
+    leaves = [t.clone().requires_grad_(True) for t in (qd, kd, vd)]
+    out = bd.squad_attention(*leaves, grid, window)
+    out.backward(dod)
+    ref = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    ref_g = bd.squad_attn_bwd(qd, kd, vd, ref, dod, grid, window)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref)
+    assert all(torch.equal(t.grad, g) for t, g in zip(leaves, ref_g))
