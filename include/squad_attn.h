@@ -322,7 +322,7 @@ int squad_attn_last_hip_error(void);
 
 /* Version of this ABI (bumped on any change; 2 adds the padded entry points,
  * the backward and SQUAD_ERR_WORKSPACE; 3 the saved-activation forward and
- * backward). */
+ * backward, and the padded workspace's region for Y). */
 int squad_attn_abi_version(void);
 
 #ifdef __cplusplus
