@@ -139,3 +139,25 @@ def test_padded_split_long_windows():
     run_padded((21, 30, 52, 21, 3, 5), "bf16", heads=4, d=128, seed=11)
     # m = 400 with 8 heads: 24 local problems of 25 tiles (grid padded to 5x24x10), two query parts
     run_padded((5, 17, 10, 5, 8, 10), "bf16", heads=8, d=128, seed=12)
+
+
+def test_padded_long_global_pass_full_grid_sampled_heads():
+    # the window-rule sweep's largest grid (1.3B aspect, 21x67x116, window 21x4x5, padded to
+    # 21x68x120): 408 windows of 420 tokens; the global pass reads Y from the workspace and runs in
+    # two query parts, the local pass too (not in place); two heads against the oracle
+    import torch
+    T, Hs, Ws, wt, wh, ww = 21, 67, 116, 21, 4, 5
+    heads, d = 4, 128
+    n = T * Hs * Ws
+    log(f"case padded full grid {T}x{Hs}x{Ws} window {wt}x{wh}x{ww} heads={heads}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    qd, kd, vd = (torch.randn(1, n, heads, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(3))
+    out = bd.squad_attn_fwd_padded(qd, kd, vd, (T, Hs, Ws), (wt, wh, ww))
+    torch.cuda.synchronize()
+    for h in (0, 3):
+        q, k, v = (to_f64(t[0, :, h, :]) for t in (qd, kd, vd))
+        ref = so.squad_head_padded(q, k, v, (T, Hs, Ws), (wt, wh, ww))
+        assert_close(to_f64(out[0, :, h, :]), ref, "bf16", f"padded {T}x{Hs}x{Ws} h={h}")
+    del qd, kd, vd, out
+    torch.cuda.empty_cache()
