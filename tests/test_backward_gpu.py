@@ -113,6 +113,25 @@ def test_backward_deterministic():
     assert all(torch.equal(x, y) for x, y in zip(a, b))
 
 
+def test_backward_cfg_pair_second_batch_element():
+    # the 14B CFG pair (B = 2, 40 heads, m = 336): a head of the second batch element
+    import torch
+    w = wl.WORKLOADS["wan14b_4x_cfg"]
+    log("case bwd workload=wan14b_4x_cfg (generating inputs)")
+    qd, kd, vd = wl.device_inputs(w, seed=0)
+    dod = wl.device_inputs(w, seed=1)[0]
+    grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)
+    out = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    dq, dk, dv = bd.squad_attn_bwd(qd, kd, vd, out, dod, grid, window)
+    torch.cuda.synchronize()
+    table = so.window_slot_table(*grid, *window)
+    q, k, v = wl.head_slices_f64(w, 1, 39)
+    ref = so.squad_backward_head(q, k, v, to_f64(dod[1, :, 39, :]), table)
+    check_grads([to_f64(t[1, :, 39, :]) for t in (dq, dk, dv)], ref, "bf16", "wan14b_4x_cfg b=1 h=39")
+    del qd, kd, vd, dod, out, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
 def test_backward_long_windows_sampled_heads():
     # the 4x 5B block: m = 336 (three groups of query / key tiles per window), N_w = 220
     import torch
