@@ -78,6 +78,14 @@ def test_backward_small(geo, dtype):
     run_bwd(geo, dtype)
 
 
+@pytest.mark.parametrize("geo", [(3, 4, 4, 3, 4, 4), (3, 4, 4, 1, 1, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_degenerate_windows(geo, dtype):
+    # one window spanning the grid (the global pass over a single row: P = 1, its dS = 0) and
+    # single-token windows (the local pass is the identity): problems of length 1 in one pass
+    run_bwd(geo, dtype, heads=2, d=64, seed=51)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_backward_head_dim_128_batch(dtype):
     run_bwd((3, 8, 10, 3, 2, 5), dtype, B=2, heads=3, d=128, seed=4)
