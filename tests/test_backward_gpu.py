@@ -265,3 +265,42 @@ def test_autograd_wrapper_matches_entry_points(dtype):
     torch.cuda.synchronize()
     assert torch.equal(out.detach(), ref)
     assert all(torch.equal(t.grad, g) for t, g in zip(leaves, ref_g))
+
+
+@pytest.mark.parametrize("saved", [False, True])
+def test_graph_capture_backward_replays_match_eager(saved):
+    # the backward enqueues kernels only (its workspace is the caller's), so it can be captured;
+    # every replay, with eager work and synchronisation between replays, reproduces the eager result
+    import torch
+    T, Hs, Ws, wt, wh, ww = 3, 10, 12, 3, 2, 2
+    grid, window = (T, Hs, Ws), (wt, wh, ww)
+    B, heads, d = 1, 4, 128
+    q, k, v = wl.random_geometry_inputs(B, heads, T * Hs * Ws, d, "bf16", seed=61)
+    do = wl.random_geometry_inputs(B, heads, T * Hs * Ws, d, "bf16", seed=62)[0]
+    qd, kd, vd, dod = host_to_device((q, k, v, do), "bf16")
+    out, y, lse = bd.squad_attn_fwd_save(qd, kd, vd, grid, window)
+    need = (bd.squad_attn_bwd_saved_workspace_bytes if saved else bd.squad_attn_bwd_workspace_bytes)(
+        B, heads, T, Hs, Ws, wt, wh, ww, d, bd.SQUAD_BF16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    grads = [torch.empty_like(qd) for _ in range(3)]
+
+    def run():
+        if saved:
+            bd.squad_attn_bwd_saved(qd, kd, vd, out, dod, y, lse, grid, window, *grads, workspace=ws)
+        else:
+            bd.squad_attn_bwd(qd, kd, vd, out, dod, grid, window, *grads, workspace=ws)
+
+    run()  # eager, and the warm-up outside capture
+    torch.cuda.synchronize()
+    eager = [g.clone() for g in grads]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for i in range(4):
+        for g in grads:
+            g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(g, e) for g, e in zip(grads, eager)), f"replay {i}"
+        bd.squad_attn_fwd(qd, kd, vd, grid, window)  # eager work between replays
+        torch.cuda.synchronize()
