@@ -192,6 +192,35 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
         f.write("| kernel | HBM read (MB) | HBM write (MB) | total (MB) | algorithmic (MB) | ratio | "
                 "trace avg (us) | GB/s |\n|---|---|---|---|---|---|---|---|\n")
         f.write("\n".join(lines) + "\n")
+    # the backward's two kernels (the same runs time squad_attn_bwd and squad_attn_bwd_saved):
+    # algorithmic bytes in tensor-sizes T = B*n*heads*d elements, per-row arrays not counted --
+    # the global pass's backward reads q, k, Y, O, dO and writes dY and its dq, dk contributions
+    # (8 T); the local pass's reads q, k, v, dY and those contributions and writes dq, dk, dv (9 T)
+    tensor = w.B * w.n * w.heads * w.d * esize
+    blines = []
+    for kernel, alg, what in (("squad_bwd_pass_bf16<128, false", 8 * tensor, "global pass"),
+                              ("squad_bwd_pass_bf16<128, true", 9 * tensor, "local pass")):
+        fk = next((k for k in fetch if k.startswith(kernel)), None)
+        wk = next((k for k in write if k.startswith(kernel)), None)
+        st = next((s for s in stats if s[0].startswith(kernel)), None)
+        if fk is None or wk is None or st is None:
+            continue
+        rd = fetch[fk][0] * fetch_scale * 1024
+        wr = write[wk][0] * write_scale * 1024
+        blines.append(f"| {fk} ({what}) | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} | "
+                      f"{alg / 1e6:.1f} | {(rd + wr) / alg:.3f} | {st[2]:.1f} | {(rd + wr) / st[2] / 1e3:.0f} |")
+    if blines:
+        with open(os.path.join(ROOT, "profiles", f"hbm_traffic_squad_backward_{w.name}.md"), "w") as f:
+            f.write(f"# HBM traffic per launch: SQuad-Attention backward kernels, {title}\n\n")
+            f.write("From the same two counter runs as the passes' summary (the runs time squad_attn_bwd "
+                    "and squad_attn_bwd_saved after the forward), scaled the same way:\n\n```\n"
+                    + PROFILE_COMMANDS["fetch"] + "\n" + PROFILE_COMMANDS["write"] + "\n```\n\n")
+            f.write("Algorithmic bytes: the global pass's backward reads q, k, Y, O and dO and writes dY and "
+                    "its dq, dk contributions (8 tensor-sizes); the local pass's reads q, k, v, dY and those "
+                    "contributions and writes dq, dk, dv (9); per-row float32 arrays not counted.\n\n")
+            f.write("| kernel | HBM read (MB) | HBM write (MB) | total (MB) | algorithmic (MB) | ratio | "
+                    "trace avg (us) | GB/s |\n|---|---|---|---|---|---|---|---|\n")
+            f.write("\n".join(blines) + "\n")
 
 
 # Backbones of the FLOP-conformance sweep: native latent grid (81 frames, T = 21)
