@@ -374,6 +374,306 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
     }
 }
 
+// One-sweep variant, for problems of at most NW key tiles whose rows'
+// log-sum-exp and D are given (the local pass).  Every wave owns one 16-key
+// tile (its K and V rows in registers, and K also written whole into LDS in
+// the transposing layout); one pass over Q and dO in 32-row blocks
+// accumulates dK^T and dV^T as the key sweep above does.  Per block the
+// waves' dS tiles meet in LDS (row-major over the block's queries, double
+// buffered), and during the next block's step the first D/16 waves form the
+// block's dQ^T = K^T dS^T from them (one query half and one d-tile pair each)
+// and store it: every input row is read from memory once, and one barrier
+// per block orders both the streamed rows and dS.
+template <int D, int NW, int PD>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : 2))) void squad_bwd_onesweep_bf16(
+    PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const uint16_t* __restrict__ dop, const uint16_t* __restrict__ addq, const uint16_t* __restrict__ addk,
+    uint16_t* __restrict__ dqp, uint16_t* __restrict__ dkp, uint16_t* __restrict__ dvp,
+    const float* __restrict__ lse_in, const float* __restrict__ dd_in, float c_log2, float scale) {
+    using G = BlockGeo<D>;
+    static_assert(NW % 2 == 0 && NW >= D / 16, "one key tile per wave, a dQ unit per wave");
+    constexpr int KMAX = 16 * NW;     // keys (and query rows) a workgroup covers
+    constexpr int KBLK = KMAX / BR;   // 32-row K blocks kept in LDS
+    // dS rows (queries) padded by 16 bytes: the dQ operand fetch (16 rows, two
+    // 8-byte pieces per 32 lanes) then covers every bank once
+    constexpr int DSTR = KMAX + 8;
+    constexpr int NU = D / 16;        // dQ units: 2 query halves x DT/2 d-tile pairs
+    __shared__ __attribute__((aligned(16))) uint16_t rowA[2][BR * G::KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t rowB[2][BR * G::KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t trA[2][BR * G::VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t trB[2][BR * G::VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t ktr[KBLK * BR * G::VSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t dsb[2][BR * DSTR];
+    __shared__ float lse[KMAX], dd[KMAX];
+    __shared__ int tab[KMAX];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int li = lane & 15;
+    const int lg = lane >> 4;
+    const int L = g.L;
+    const int NB = (L + BR - 1) / BR;
+    const int row_stride = g.heads * D;
+
+    const ProblemIndex pr = decode_problem(g, blockIdx.x);
+    const int base = g.global ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
+    // the problem's (b, h) slice: rows are 32-bit element offsets from it
+    // (the launcher requires n * heads * D < 2^31)
+    const int64_t bh = (int64_t)pr.b * g.n * row_stride + (int64_t)pr.h * D;
+    qp += bh;
+    kp += bh;
+    vp += bh;
+    dop += bh;
+    if (addq) addq += bh;
+    if (addk) addk += bh;
+    dqp += bh;
+    dkp += bh;
+    dvp += bh;
+    const int64_t bh_row = bh / D;  // per-row arrays: [B, n, heads]
+    lse_in += bh_row;
+    dd_in += bh_row;
+    for (int r = tid; r < L; r += blockDim.x) tab[r] = g.global ? win_origin(g, r) : slot_offset(g, r);
+    // query rows past L up to the last block's end: log-sum-exp +inf and D 0
+    for (int r = L + tid; r < NB * BR; r += blockDim.x) {
+        lse[r] = INFINITY;
+        dd[r] = 0.0f;
+    }
+    __syncthreads();
+    auto row = [&](int r) -> int { return (base + tab[min(r, L - 1)]) * row_stride; };
+
+    // ---- loader: block st of Q (row and transposed layouts) and of dO (both)
+    // PD steps in flight (staging registers); the step loop is unrolled by UN
+    // (even, so that the LDS buffers alternate by step parity at compile time)
+    // over NB live steps plus the dQ-only step
+    constexpr int UN = PD < 2 ? 2 : PD;
+    static_assert(UN % PD == 0 && UN % 2 == 0, "staging slots and buffer parity per unrolled step");
+    const int nsteps = (NB + 1 + UN - 1) / UN * UN;
+    const bool stager = tid < G::NCH;
+    const int ch = stager ? tid : G::NCH - 1;
+    const int ld_row = ch / G::KC;
+    const int ld_col = (ch % G::KC) * 8;
+    int ld_s = 0;
+    u32x4 sx1[PD], sx2[PD];
+    auto issue = [&](u32x4& x1, u32x4& x2) {
+        const bool dead = ld_s >= NB;
+        const int a = row(ld_s * BR + ld_row) + ld_col;
+        x1 = *reinterpret_cast<const u32x4*>(qp + (dead ? 0 : a));
+        x2 = *reinterpret_cast<const u32x4*>(dop + (dead ? 0 : a));
+        ++ld_s;
+    };
+    const int t_put = v_chunk_offset<D>(ld_row, ld_col / 8);
+    const bool t_swap = v_halves_swapped<D>(ld_row);
+    auto put = [&](const u32x4& x1, const u32x4& x2, int buf) {
+        if (!stager) return;
+        *reinterpret_cast<u32x4*>(&rowA[buf][ld_row * G::KSTR + ld_col]) = x1;
+        *reinterpret_cast<u32x4*>(&trA[buf][t_put]) = t_swap ? u32x4{x1.z, x1.w, x1.x, x1.y} : x1;
+        *reinterpret_cast<u32x4*>(&rowB[buf][ld_row * G::KSTR + ld_col]) = x2;
+        *reinterpret_cast<u32x4*>(&trB[buf][t_put]) = t_swap ? u32x4{x2.z, x2.w, x2.x, x2.y} : x2;
+    };
+    auto row_op = [&](const uint16_t* rb, int half, int s) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(&rb[(half * 16 + li) * G::KSTR + (4 * s + lg) * 8]);
+    };
+    const int vr = v_fetch_row(li, lg);
+    auto tr_op = [&](const uint16_t* tb, int dt) -> bf16x8 {
+        const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&tb[off]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&tb[off + 16 * G::VSTR]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+    };
+    // the same fetch at a given lane offset (rows off and off + 16 of block tb)
+    auto tr_at = [&](uint16_t* tb, int off) -> bf16x8 {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&tb[off]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&tb[off + 16 * G::VSTR]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        return __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int u = 0; u < PD; ++u) issue(sx1[u], sx2[u]);
+
+    // ---- this wave's key tile: rows, whole-problem K in LDS, per-row sums --
+    // Tiles past the last K block take no part; tiles inside it but past L
+    // (clamped rows) take part with probabilities forced to 0.
+    const int kt = wave;
+    const bool kact = kt < 2 * NB;
+    const bool kdead = kt * 16 + li >= L;
+    for (int r = tid; r < L; r += blockDim.x) {
+        const int ri = row(r) / D;
+        lse[r] = lse_in[ri];
+        dd[r] = dd_in[ri];
+    }
+    // The wave's K rows live only in LDS (the score operand is read back from
+    // the transposing layout, halves restored): registers are kept for V.
+    const int kr = 16 * (kt & 1) + li;
+    const bool ksw = v_halves_swapped<D>(kr);
+    uint16_t* const kblk = &ktr[(kt >> 1) * BR * G::VSTR];
+    bf16x8 vreg[G::KS];
+    if (kact) {
+        const int a = row(kt * 16 + li);
+        u32x4 kx[G::KS];
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
+            kx[s] = *reinterpret_cast<const u32x4*>(kp + a + (4 * s + lg) * 8);
+            vreg[s] = *reinterpret_cast<const bf16x8*>(vp + a + (4 * s + lg) * 8);
+        }
+#pragma unroll
+        for (int s = 0; s < G::KS; ++s) {
+            const u32x4 x = kx[s];
+            *reinterpret_cast<u32x4*>(&kblk[v_chunk_offset<D>(kr, 4 * s + lg)]) = ksw ? u32x4{x.z, x.w, x.x, x.y} : x;
+        }
+    }
+    auto k_op = [&](int s) -> bf16x8 {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(&kblk[v_chunk_offset<D>(kr, 4 * s + lg)]);
+        return __builtin_bit_cast(bf16x8, ksw ? u32x4{x.z, x.w, x.x, x.y} : x);
+    };
+    f32x4 dkacc[G::DT], dvacc[G::DT];
+#pragma unroll
+    for (int dt = 0; dt < G::DT; ++dt) dkacc[dt] = dvacc[dt] = zero;
+
+    // dQ unit of this wave: query half uh, d tiles 2 up, 2 up + 1
+    const bool dq_wave = wave < NU;
+    const int uh = wave & 1, up = wave >> 1;
+    int st = 0;
+    for (int s0 = 0; s0 < nsteps; s0 += UN) {
+#pragma unroll
+        for (int u = 0; u < UN; ++u, ++st) {
+            if (st > NB) break;  // uniform
+            // the other pass's contribution to the dQ rows formed in this step
+            const int qr = (st - 1) * BR + 16 * uh + li;
+            const bool qout = dq_wave && st >= 1 && qr < L;
+            const int qa = qout ? row(qr) + 32 * up + 8 * lg : 0;
+            bf16x8 aq;
+            if (addq && qout) aq = *reinterpret_cast<const bf16x8*>(addq + qa);
+            put(sx1[u % PD], sx2[u % PD], u & 1);
+            issue(sx1[u % PD], sx2[u % PD]);
+            __syncthreads();
+            if (st < NB && kact) {
+                f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    const bf16x8 kop = k_op(s);
+                    sa = mfma(row_op(rowA[u & 1], 0, s), kop, sa);  // S (block queries x this wave's keys)
+                    sb = mfma(row_op(rowA[u & 1], 1, s), kop, sb);
+                    pa = mfma(row_op(rowB[u & 1], 0, s), vreg[s], pa);  // dP
+                    pb = mfma(row_op(rowB[u & 1], 1, s), vreg[s], pb);
+                }
+                float pr0[4], pr1[4], ds0[4], ds1[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int q0 = st * BR + 4 * lg + i, q1 = q0 + 16;
+                    const float e0 = kdead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(sa[i], c_log2, -lse[q0]));
+                    const float e1 = kdead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(sb[i], c_log2, -lse[q1]));
+                    pr0[i] = e0;
+                    pr1[i] = e1;
+                    ds0[i] = e0 * (pa[i] - dd[q0]);
+                    ds1[i] = e1 * (pb[i] - dd[q1]);
+                }
+                const bf16x8 pp = pack8(pr0, pr1), dsp = pack8(ds0, ds1);
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt) {
+                    dvacc[dt] = mfma(tr_op(trB[u & 1], dt), pp, dvacc[dt]);
+                    dkacc[dt] = mfma(tr_op(trA[u & 1], dt), dsp, dkacc[dt]);
+                }
+                // dS of this block: query rows 4lg + i and 16 + 4lg + i, key 16 kt + li
+                // (the 16-bit halves of the packed words: a bit cast of one
+                // bf16 element of the vector was compiled as element 0 for all)
+                uint16_t* db = &dsb[u & 1][kt * 16 + li];
+                const u32x4 w = __builtin_bit_cast(u32x4, dsp);
+                const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    db[(4 * lg + i) * DSTR] = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
+                    db[(16 + 4 * lg + i) * DSTR] = (uint16_t)(wv[2 + (i >> 1)] >> (16 * (i & 1)));
+                }
+            }
+            if (st >= 1 && dq_wave) {
+                // dQ^T of the previous block: contraction over its keys in 32-key steps.
+                // The lane's LDS addresses are rebuilt here from a laundered lane
+                // index, so that they are not held in registers across the step
+                // loop (where they would be spilled and reloaded, and each reload
+                // waits for every load in flight).
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int qli = ln & 15, qlg = ln >> 4;
+                const uint16_t* db = &dsb[(u + 1) & 1][(16 * uh + qli) * DSTR + 4 * qlg];
+                const int qvr = v_fetch_row(qli, qlg);
+                const int o0 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up), 0);
+                const int o1 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up + 1), 1);
+                f32x4 a0 = zero, a1 = zero;
+                for (int ks = 0; ks < NB; ++ks) {
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(db + 32 * ks);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(db + 32 * ks + 16);
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                    uint16_t* kb = &ktr[ks * BR * G::VSTR];
+                    a0 = mfma(tr_at(kb, o0), bop, a0);
+                    a1 = mfma(tr_at(kb, o1), bop, a1);
+                }
+                if (qout) {
+                    float o[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        o[i] = a0[i] * scale;
+                        o[4 + i] = a1[i] * scale;
+                    }
+                    if (addq) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) o[e] += (float)aq[e];
+                    }
+                    bf16x8 b;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) b[e] = static_cast<__bf16>(o[e]);
+                    *reinterpret_cast<bf16x8*>(dqp + qa) = b;
+                }
+            }
+        }
+    }
+
+    // ---- dK, dV of this wave's tile ------------------------------------------
+    const int r = kt * 16 + li;
+    if (!kact || r >= L) return;
+    const int a = row(r) + 8 * lg;
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p) {
+        float ok[8], ov[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ok[i] = dkacc[2 * p][i] * scale;
+            ok[4 + i] = dkacc[2 * p + 1][i] * scale;
+            ov[i] = dvacc[2 * p][i];
+            ov[4 + i] = dvacc[2 * p + 1][i];
+        }
+        if (addk) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(addk + a + 32 * p);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ok[e] += (float)x[e];
+        }
+        bf16x8 bk, bv;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            bk[e] = static_cast<__bf16>(ok[e]);
+            bv[e] = static_cast<__bf16>(ov[e]);
+        }
+        *reinterpret_cast<bf16x8*>(dkp + a + 32 * p) = bk;
+        *reinterpret_cast<bf16x8*>(dvp + a + 32 * p) = bv;
+    }
+}
+
+template <int D, int NW, int PD>
+hipError_t launch_onesweep(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
+    const float scale = 1.0f / __builtin_sqrtf((float)D);
+    const float c_log2 = 1.4426950408889634f * scale;
+    hipLaunchKernelGGL((squad_bwd_onesweep_bf16<D, NW, PD>), dim3(g.nprob), dim3(64 * NW), 0, st, g,
+                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                       static_cast<const uint16_t*>(a.vals), static_cast<const uint16_t*>(a.dout),
+                       static_cast<const uint16_t*>(a.addq), static_cast<const uint16_t*>(a.addk),
+                       static_cast<uint16_t*>(a.dq), static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dvals),
+                       a.lse, a.dd_in, c_log2, scale);
+    return hipGetLastError();
+}
+
 template <int D, bool HASLSE, int NW, int PD>
 hipError_t launch_nw(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
     const float scale = 1.0f / __builtin_sqrtf((float)D);
@@ -401,6 +701,11 @@ hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream) {
+    const int tiles = (g.L + 15) / 16;
+    if (a.lse && a.dd_in && !a.vdot && tiles <= 12 && g.n * g.heads * d < (int64_t(1) << 31)) {
+        if (tiles <= 8) return d == 128 ? launch_onesweep<128, 8, 4>(g, a, stream) : launch_onesweep<64, 8, 4>(g, a, stream);
+        return d == 128 ? launch_onesweep<128, 12, 1>(g, a, stream) : launch_onesweep<64, 12, 2>(g, a, stream);
+    }
     if (a.lse) return d == 128 ? launch_d<128, true>(g, a, stream) : launch_d<64, true>(g, a, stream);
     return d == 128 ? launch_d<128, false>(g, a, stream) : launch_d<64, false>(g, a, stream);
 }

@@ -61,7 +61,9 @@ def run_bwd(geo, dtype, B=1, heads=2, d=64, seed=0):
 
 
 # one block, ragged blocks, several blocks, more query tiles than waves, long
-# windows (m = 336 as the 4x workloads), many windows
+# windows (m = 336 as the 4x workloads), many windows; local windows of 7, 10
+# and 12 key tiles (m = 100, 150 ragged, 192 whole: the one-sweep local
+# backward on 8 and 12 waves, the latter with every K block of LDS in use)
 GEOS = [
     (3, 4, 4, 3, 2, 2),
     (2, 6, 8, 1, 3, 4),
@@ -69,6 +71,9 @@ GEOS = [
     (3, 10, 12, 3, 5, 4),
     (21, 8, 8, 21, 4, 4),
     (2, 24, 20, 1, 1, 2),
+    (5, 8, 10, 5, 4, 5),
+    (3, 10, 20, 3, 5, 10),
+    (3, 8, 16, 3, 8, 8),
 ]
 
 
