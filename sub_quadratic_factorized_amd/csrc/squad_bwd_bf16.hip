@@ -439,6 +439,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
         lse[r] = INFINITY;
         dd[r] = 0.0f;
     }
+    // K blocks and dS key columns past the last block: zero (the dQ product
+    // runs over all KBLK blocks; no wave writes these)
+    for (int i = NB * BR * G::VSTR + tid * 8; i < KBLK * BR * G::VSTR; i += blockDim.x * 8)
+        *reinterpret_cast<u32x4*>(&ktr[i]) = u32x4{0u, 0u, 0u, 0u};
+    for (int i = tid; i < 2 * BR * (KMAX - NB * BR); i += blockDim.x) {
+        const int b = i / (BR * (KMAX - NB * BR)), j = i - b * (BR * (KMAX - NB * BR));
+        const int q = j / (KMAX - NB * BR), c = NB * BR + j - q * (KMAX - NB * BR);
+        dsb[b][q * DSTR + c] = 0;
+    }
     __syncthreads();
     auto row = [&](int r) -> int { return (base + tab[min(r, L - 1)]) * row_stride; };
 
@@ -536,6 +545,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
     // dQ unit of this wave: query half uh, d tiles 2 up, 2 up + 1
     const bool dq_wave = wave < NU;
     const int uh = wave & 1, up = wave >> 1;
+    // The dQ rows' addend load and store are buffer operations that every
+    // wave issues at every step (lanes without a row use an offset past the
+    // descriptor's end: the load returns zeros, the store is dropped), so the
+    // count of memory operations between a step's loads and their use is the
+    // same on every path: a wait for the streamed rows then need not also
+    // wait for the previous step's dQ stores to complete.  The descriptors
+    // cover the rest of the batch element from the (b, h) slice (under 2^31
+    // bytes: the launcher requires n * heads * D < 2^30).
+    const int slice_bytes = (int)((g.n * g.heads * D - (int64_t)pr.h * D) * 2);
+    const __amdgpu_buffer_rsrc_t raq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(addq ? addq : dqp), 0, addq ? slice_bytes : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdq = __builtin_amdgcn_make_buffer_rsrc(dqp, 0, slice_bytes, 0x00020000);
+    constexpr uint32_t kNoRow = 0x80000000u;
     int st = 0;
     for (int s0 = 0; s0 < nsteps; s0 += UN) {
 #pragma unroll
@@ -544,9 +566,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
             // the other pass's contribution to the dQ rows formed in this step
             const int qr = (st - 1) * BR + 16 * uh + li;
             const bool qout = dq_wave && st >= 1 && qr < L;
-            const int qa = qout ? row(qr) + 32 * up + 8 * lg : 0;
-            bf16x8 aq;
-            if (addq && qout) aq = *reinterpret_cast<const bf16x8*>(addq + qa);
+            const uint32_t qoff = qout ? (uint32_t)(row(qr) + 32 * up + 8 * lg) * 2u : kNoRow;
+            const bf16x8 aq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(raq, qoff, 0, 0));
             put(sx1[u % PD], sx2[u % PD], u & 1);
             issue(sx1[u % PD], sx2[u % PD]);
             __syncthreads();
@@ -589,6 +610,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                     db[(16 + 4 * lg + i) * DSTR] = (uint16_t)(wv[2 + (i >> 1)] >> (16 * (i & 1)));
                 }
             }
+            f32x4 a0 = zero, a1 = zero;
             if (st >= 1 && dq_wave) {
                 // dQ^T of the previous block: contraction over its keys in 32-key steps.
                 // The lane's LDS addresses are rebuilt here from a laundered lane
@@ -602,8 +624,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                 const int qvr = v_fetch_row(qli, qlg);
                 const int o0 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up), 0);
                 const int o1 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up + 1), 1);
-                f32x4 a0 = zero, a1 = zero;
-                for (int ks = 0; ks < NB; ++ks) {
+                // all KBLK key blocks (those past the problem's last are zero), so
+                // that the fetches of later blocks can be issued early
+#pragma unroll
+                for (int ks = 0; ks < KBLK; ++ks) {
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(db + 32 * ks);
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(db + 32 * ks + 16);
                     const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
@@ -611,22 +635,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                     a0 = mfma(tr_at(kb, o0), bop, a0);
                     a1 = mfma(tr_at(kb, o1), bop, a1);
                 }
-                if (qout) {
-                    float o[8];
+            }
+            {
+                bf16x8 b;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        o[i] = a0[i] * scale;
-                        o[4 + i] = a1[i] * scale;
-                    }
-                    if (addq) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) o[e] += (float)aq[e];
-                    }
-                    bf16x8 b;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) b[e] = static_cast<__bf16>(o[e]);
-                    *reinterpret_cast<bf16x8*>(dqp + qa) = b;
+                for (int i = 0; i < 4; ++i) {
+                    b[i] = static_cast<__bf16>(fmaf(a0[i], scale, (float)aq[i]));
+                    b[4 + i] = static_cast<__bf16>(fmaf(a1[i], scale, (float)aq[4 + i]));
                 }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rdq, qoff, 0, 0);
             }
         }
     }
@@ -702,7 +719,7 @@ hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream) {
     const int tiles = (g.L + 15) / 16;
-    if (a.lse && a.dd_in && !a.vdot && tiles <= 12 && g.n * g.heads * d < (int64_t(1) << 31)) {
+    if (a.lse && a.dd_in && !a.vdot && tiles <= 12 && g.n * g.heads * d < (int64_t(1) << 30)) {
         if (tiles <= 8) return d == 128 ? launch_onesweep<128, 8, 4>(g, a, stream) : launch_onesweep<64, 8, 4>(g, a, stream);
         return d == 128 ? launch_onesweep<128, 12, 1>(g, a, stream) : launch_onesweep<64, 12, 2>(g, a, stream);
     }
