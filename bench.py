@@ -199,6 +199,7 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
     tensor = w.B * w.n * w.heads * w.d * esize
     blines = []
     for kernel, alg, what in (("squad_bwd_pass_bf16<128, false", 8 * tensor, "global pass"),
+                              ("squad_bwd_onesweep_bf16<128", 9 * tensor, "local pass, one sweep"),
                               ("squad_bwd_pass_bf16<128, true", 9 * tensor, "local pass")):
         fk = next((k for k in fetch if k.startswith(kernel)), None)
         wk = next((k for k in write if k.startswith(kernel)), None)

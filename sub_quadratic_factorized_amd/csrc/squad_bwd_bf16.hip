@@ -376,14 +376,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
 
 // One-sweep variant, for problems of at most NW key tiles whose rows'
 // log-sum-exp and D are given (the local pass).  Every wave owns one 16-key
-// tile (its K and V rows in registers, and K also written whole into LDS in
-// the transposing layout); one pass over Q and dO in 32-row blocks
+// tile: its V rows in registers, its K rows in LDS, where K is kept whole in
+// the transposing layout.  One pass over Q and dO in 32-row blocks
 // accumulates dK^T and dV^T as the key sweep above does.  Per block the
 // waves' dS tiles meet in LDS (row-major over the block's queries, double
-// buffered), and during the next block's step the first D/16 waves form the
-// block's dQ^T = K^T dS^T from them (one query half and one d-tile pair each)
-// and store it: every input row is read from memory once, and one barrier
-// per block orders both the streamed rows and dS.
+// buffered), and at the start of the next block's step the first D/16 waves
+// form the block's dQ^T = K^T dS^T from them (one query half and one d-tile
+// pair each) and store it, while the other waves begin that step's scores:
+// every input row is read from memory once, and one barrier per block orders
+// both the streamed rows and dS.  One step in flight (PD = 1) on 12 waves:
+// with two, registers spill, and every reload of a spilled value waits for
+// all loads in flight.
 template <int D, int NW, int PD>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 ? 3 : 2))) void squad_bwd_onesweep_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -571,6 +574,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
             put(sx1[u % PD], sx2[u % PD], u & 1);
             issue(sx1[u % PD], sx2[u % PD]);
             __syncthreads();
+            f32x4 a0 = zero, a1 = zero;
+            if (st >= 1 && dq_wave) {
+                // dQ^T of the previous block: contraction over its keys in 32-key steps.
+                // The lane's LDS addresses are rebuilt here from a laundered lane
+                // index, so that they are not held in registers across the step
+                // loop (where they would be spilled and reloaded, and each reload
+                // waits for every load in flight).
+                int ln = lane;
+                asm volatile("" : "+v"(ln));
+                const int qli = ln & 15, qlg = ln >> 4;
+                const uint16_t* db = &dsb[(u + 1) & 1][(16 * uh + qli) * DSTR + 4 * qlg];
+                const int qvr = v_fetch_row(qli, qlg);
+                const int o0 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up), 0);
+                const int o1 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up + 1), 1);
+                // all KBLK key blocks (those past the problem's last are zero), so
+                // that the fetches of later blocks can be issued early
+#pragma unroll
+                for (int ks = 0; ks < KBLK; ++ks) {
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(db + 32 * ks);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(db + 32 * ks + 16);
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                    uint16_t* kb = &ktr[ks * BR * G::VSTR];
+                    a0 = mfma(tr_at(kb, o0), bop, a0);
+                    a1 = mfma(tr_at(kb, o1), bop, a1);
+                }
+            }
+            {
+                bf16x8 b;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    b[i] = static_cast<__bf16>(fmaf(a0[i], scale, (float)aq[i]));
+                    b[4 + i] = static_cast<__bf16>(fmaf(a1[i], scale, (float)aq[4 + i]));
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rdq, qoff, 0, 0);
+            }
             if (st < NB && kact) {
                 f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
 #pragma unroll
@@ -609,41 +647,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                     db[(4 * lg + i) * DSTR] = (uint16_t)(wv[i >> 1] >> (16 * (i & 1)));
                     db[(16 + 4 * lg + i) * DSTR] = (uint16_t)(wv[2 + (i >> 1)] >> (16 * (i & 1)));
                 }
-            }
-            f32x4 a0 = zero, a1 = zero;
-            if (st >= 1 && dq_wave) {
-                // dQ^T of the previous block: contraction over its keys in 32-key steps.
-                // The lane's LDS addresses are rebuilt here from a laundered lane
-                // index, so that they are not held in registers across the step
-                // loop (where they would be spilled and reloaded, and each reload
-                // waits for every load in flight).
-                int ln = lane;
-                asm volatile("" : "+v"(ln));
-                const int qli = ln & 15, qlg = ln >> 4;
-                const uint16_t* db = &dsb[(u + 1) & 1][(16 * uh + qli) * DSTR + 4 * qlg];
-                const int qvr = v_fetch_row(qli, qlg);
-                const int o0 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up), 0);
-                const int o1 = v_half_offset<D>(qvr, v_fetch_col(qli, 2 * up + 1), 1);
-                // all KBLK key blocks (those past the problem's last are zero), so
-                // that the fetches of later blocks can be issued early
-#pragma unroll
-                for (int ks = 0; ks < KBLK; ++ks) {
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(db + 32 * ks);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(db + 32 * ks + 16);
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                    uint16_t* kb = &ktr[ks * BR * G::VSTR];
-                    a0 = mfma(tr_at(kb, o0), bop, a0);
-                    a1 = mfma(tr_at(kb, o1), bop, a1);
-                }
-            }
-            {
-                bf16x8 b;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    b[i] = static_cast<__bf16>(fmaf(a0[i], scale, (float)aq[i]));
-                    b[4 + i] = static_cast<__bf16>(fmaf(a1[i], scale, (float)aq[4 + i]));
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, b), rdq, qoff, 0, 0);
             }
         }
     }
@@ -719,6 +722,8 @@ hipError_t launch_d(const PassGeom& g, const BwdArgs& a, hipStream_t st) {
 
 hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipStream_t stream) {
     const int tiles = (g.L + 15) / 16;
+    // the local pass (log-sum-exp and D given) of windows up to 12 key tiles:
+    // the one-sweep kernel (32-bit row offsets within a batch element)
     if (a.lse && a.dd_in && !a.vdot && tiles <= 12 && g.n * g.heads * d < (int64_t(1) << 30)) {
         if (tiles <= 8) return d == 128 ? launch_onesweep<128, 8, 4>(g, a, stream) : launch_onesweep<64, 8, 4>(g, a, stream);
         return d == 128 ? launch_onesweep<128, 12, 1>(g, a, stream) : launch_onesweep<64, 12, 2>(g, a, stream);
