@@ -96,6 +96,14 @@ def test_backward_head_dim_128_batch(dtype):
     run_bwd((3, 8, 10, 3, 2, 5), dtype, B=2, heads=3, d=128, seed=4)
 
 
+@pytest.mark.parametrize("geo", [(3, 10, 20, 3, 5, 10), (3, 8, 16, 3, 8, 8)])
+def test_backward_one_sweep_12_waves_batch_head_dim_128(geo):
+    # local windows of 10 (ragged) and 12 key tiles at d = 128 on the second
+    # batch element too: the one-sweep local backward on 12 waves, whose rows
+    # are 32-bit offsets from each (b, h) slice
+    run_bwd(geo, "bf16", B=2, heads=3, d=128, seed=61)
+
+
 def test_backward_headline_sampled_heads():
     import torch
     w = wl.WORKLOADS["wan5b_704p"]
