@@ -34,7 +34,10 @@
 // score of -inf in a problem's last block only, and query rows there a
 // log-sum-exp of +inf and a D of 0, so their P and dS come out 0.  P and dS
 // enter their MFMAs rounded to bf16, and the other pass's contributions to dQ
-// and dK arrive in bf16; all sums are float32.
+// and dK arrive in bf16; all sums are float32.  A problem whose keys fit one
+// 16-key tile per wave and whose log-sum-exp and D are given (the local pass
+// of windows up to 12 key tiles) takes the one-sweep variant further below
+// instead: one pass over Q and dO, dQ reduced per block through LDS.
 #include "squad_internal.h"
 #include "squad_layout.h"
 #include "squad_mfma.h"
