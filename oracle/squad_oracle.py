@@ -274,12 +274,6 @@ def solve_window(T, Hs, Ws):
     return T, wh, ww
 
 
-def reflect_index(i, size):
-    """Source index of position i of an axis of length `size` extended past its
-    end by mirroring about the last element (the edge is not repeated)."""
-    return i if i < size else 2 * (size - 1) - i
-
-
 def reflect_pad_tokens(x, T, Hs, Ws, Hp, Wp):
     """[n, ...] in (t, y, x) order -> [T*Hp*Wp, ...]: the grid extended at the
     bottom and right to (T, Hp, Wp) by mirroring (reading: padding at the far
@@ -358,15 +352,15 @@ def softmax_attention_backward(q, k, v, do):
     """(dq, dk, dv) of softmax(q k^T / sqrt(d)) v over the last two axes, float64."""
     q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
     d = q.shape[-1]
-    s = q @ np.swapaxes(k, -1, -2) / math.sqrt(d)
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(d)
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=-1, keepdims=True)
-    dv = np.swapaxes(p, -1, -2) @ do
-    dp = do @ np.swapaxes(v, -1, -2)
+    dv = np.matmul(np.swapaxes(p, -1, -2), do)
+    dp = np.matmul(do, np.swapaxes(v, -1, -2))
     ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
-    dq = ds @ k / math.sqrt(d)
-    dk = np.swapaxes(ds, -1, -2) @ q / math.sqrt(d)
+    dq = np.matmul(ds, k) / math.sqrt(d)
+    dk = np.matmul(np.swapaxes(ds, -1, -2), q) / math.sqrt(d)
     return dq, dk, dv
 
 

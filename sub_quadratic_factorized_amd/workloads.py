@@ -15,8 +15,9 @@ Shapes follow the pages' workloads:
   * 4x the 5B tokens (n = 73,920, window 21x4x4) and a 14B-shaped block
     (40 heads) at the same grid, batched over a CFG pair.
 
-Value recipe (attention maps in video DiTs are sparse and heavy-tailed, with
-most mass on a few critical tokens -- paperpeel full text, sec. 1):
+Value recipe (in the pages' video models a handful of keys take most of a
+query's softmax weight -- agihunt.info summary, the paragraph on the
+observation the method starts from):
   Q, K, V ~ N(0, 1) drawn in float32; for the bf16 workloads, round(0.02 n)
   distinct token positions per batch element have their K rows multiplied by 4
   for every head; then every tensor is rounded to bf16 (round to nearest even).

@@ -130,8 +130,72 @@ def test_value_gradient_totals():
     assert np.max(np.abs(dv.sum(axis=0) - do.sum(axis=0))) < 1e-12
 
 
-def test_backward_flops():
+class _CountingNumpy:
+    """Stands in for numpy inside the oracle module: every np.matmul the oracle
+    executes adds 2 FLOPs per multiply-add of the product it actually formed
+    (each output element sums a.shape[-1] products), whatever its batch shape."""
+
+    def __init__(self):
+        self.flops = 0
+
+    def __getattr__(self, name):
+        return getattr(np, name)
+
+    def matmul(self, a, b):
+        a, b = np.asarray(a), np.asarray(b)
+        out = np.matmul(a, b)
+        self.flops += 2 * out.size * a.shape[-1]
+        return out
+
+
+COUNT_GEOS = [(2, 3, 3, 4, 4, 3, 2, 2, 8), (1, 2, 2, 6, 8, 1, 3, 4, 5), (1, 1, 4, 2, 6, 2, 1, 3, 3)]
+
+
+def counted_flops(monkeypatch, geo, seed=5):
+    """(forward, backward) FLOPs counted from the products the oracle runs: the
+    forward, and the backward less the local pass it recomputes (the forward
+    does not keep Y, and the backward's count leaves that recompute out)."""
+    B, heads, T, Hs, Ws = geo[:5]
+    d = geo[-1]
+    q, k, v, do = (rand((B, T * Hs * Ws, heads, d), seed + i) for i in range(4))
+    counter = _CountingNumpy()
+    monkeypatch.setattr(so, "np", counter)
+    so.squad_attention(q, k, v, geo)
+    fwd = counter.flops
+    counter.flops = 0
+    so.squad_backward(q, k, v, do, geo)
+    bwd_total = counter.flops
+    counter.flops = 0
+    so.local_pass(q, k, v, geo)
+    recompute = counter.flops
+    monkeypatch.undo()
+    return fwd, bwd_total - recompute
+
+
+def check_flop_counts(monkeypatch, fwd_fn, bwd_fn):
+    for geo in COUNT_GEOS:
+        fwd, bwd = counted_flops(monkeypatch, geo)
+        if fwd != fwd_fn(*geo) or bwd != bwd_fn(*geo):
+            return False
+    return True
+
+
+def test_flop_counts_match_the_products_executed(monkeypatch):
+    # the closed forms against the matmuls the oracle's two passes and their
+    # gradients actually run (five L x L x d products per attention in the
+    # backward, two in the forward), on three small geometries
+    assert check_flop_counts(monkeypatch, so.squad_flops, so.squad_backward_flops)
+    # and at the headline shape, the ratio the count implies
     assert so.squad_backward_flops(1, 24, 21, 22, 40, 21, 2, 4, 128) == 5 * 63_128_862_720 // 2
+
+
+@pytest.mark.parametrize("factor", [2, 3, 4])
+def test_flop_count_pin_catches_planted_miscounts(monkeypatch, factor):
+    # a backward counted as 2F, 3F or 4F instead of 2.5F (F the forward's
+    # count: e.g. the score recompute forgotten, the recompute of Y included,
+    # or one product too many) must fail the pin
+    mutant = lambda *geo: factor * so.squad_flops(*geo)
+    assert not check_flop_counts(monkeypatch, so.squad_flops, mutant)
 
 
 # planted mistakes in copies of the backward
