@@ -35,7 +35,7 @@ KERNEL_SOURCES = ["sub_quadratic_factorized_amd/csrc/squad_pass_bf16.hip",
                   "sub_quadratic_factorized_amd/csrc/squad_internal.h",
                   "sub_quadratic_factorized_amd/csrc/squad_layout.h"]
 # rocprofv3 runs whose CSV output --summarize-profiles turns into the files under profiles/
-PROFILE_ARGS = "--no-cpu-baseline --steps 20 --warmup 2 --kernel-iters 20 --copy-calibration-mib 512"
+PROFILE_ARGS = "--no-cpu-baseline --no-other-workloads --steps 20 --warmup 2 --kernel-iters 20 --copy-calibration-mib 512"
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d <out>/trace -o run -- python3 bench.py " + PROFILE_ARGS,
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o run -- python3 bench.py " + PROFILE_ARGS,
@@ -275,42 +275,107 @@ def run_sweep(iters: int) -> None:
         torch.cuda.empty_cache()
 
 
-def cpu_baseline(w, min_s=10.0, budget_s=25.0):
-    """The fp64 oracle on host cores over a bounded sample of the workload's heads."""
-    import numpy as np
-    from oracle import squad_oracle as so
-    from sub_quadratic_factorized_amd import workloads as wl
+def blas_description():
+    """(name, threads) of the BLAS library numpy's products run on, as threadpoolctl reports it."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = 1
+        libs = []
+    if not libs:
+        return "unknown", None
+    i = libs[0]
+    name = f"{i.get('internal_api', '?')} {i.get('version', '?')} ({os.path.basename(i.get('filepath', '?'))})"
+    return name, i.get("num_threads")
+
+
+def cpu_baseline(w, runs=3):
+    """The fp64 oracle on the host cores: the whole block (every head of batch
+    element 0) timed as 1 untimed warm-up run plus the minimum of `runs` timed
+    runs, BLAS threads set to the cores this process may run on."""
+    from oracle import squad_oracle as so
+    from sub_quadratic_factorized_amd import workloads as wl
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        limiter = None
+    blas, blas_threads = blas_description()
     table = so.window_slot_table(w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
     per_head_flops = so.squad_flops(1, 1, w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww, w.d)
-    q, k, v = wl.head_slices_f64(w, 0, 0)
-    so.squad_head(q, k, v, table)  # warm-up, untimed
-    # whole sweeps over the heads of batch element 0, repeated until ~min_s of work
-    heads_done, elapsed, sweeps = 0, 0.0, 0
-    while elapsed < min_s and elapsed < budget_s:
-        for h in range(w.heads):
-            q, k, v = wl.head_slices_f64(w, 0, h)
-            t0 = time.perf_counter()
+    heads = [wl.head_slices_f64(w, 0, h) for h in range(w.heads)]  # generated untimed
+    times = []
+    for r in range(runs + 1):
+        t0 = time.perf_counter()
+        for q, k, v in heads:
             so.squad_head(q, k, v, table)
-            elapsed += time.perf_counter() - t0
-            heads_done += 1
-            if elapsed > budget_s:
-                break
-        sweeps += 1
-    rate = heads_done * per_head_flops / elapsed / 1e12
+        if r > 0:  # run 0 is the warm-up
+            times.append(time.perf_counter() - t0)
+    if limiter is not None:
+        limiter.unregister()
+    best = min(times)
     return {
-        "value": rate,
+        "value": len(heads) * per_head_flops / best / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{heads_done} (b=0, head) slices of {w.name} ({sweeps} sweep(s) over its {w.heads} heads), "
-                  f"numpy float64, {elapsed:.2f} s of oracle time",
-        "ms_per_block_equiv": elapsed / heads_done * w.B * w.heads * 1e3,
+        "sample": f"the {w.heads} heads of batch element 0 of {w.name} (the whole block at B = 1), numpy float64; "
+                  f"1 warm-up run, then the minimum of {runs} runs",
+        "blas": blas,
+        "blas_threads": blas_threads,
+        "runs_s": times,
+        "ms_per_block_equiv": best / len(heads) * w.B * w.heads * 1e3,
     }
+
+
+def time_other_workload(name, steps=20, warmup=5, kernel_iters=10):
+    """One of the other configurations, timed like the headline (a single
+    input set: each of these sets exceeds the last-level cache on its own;
+    the tiny fp32 case is launch-bound and reported in ms only)."""
+    import torch
+    from sub_quadratic_factorized_amd import binding as bd
+    from sub_quadratic_factorized_amd import workloads as wl
+    w = wl.WORKLOADS[name]
+    grid, window = (w.T, w.Hs, w.Ws), (w.wt, w.wh, w.ww)
+    dt = bd.SQUAD_BF16 if w.dtype == "bf16" else bd.SQUAD_F32
+    flops = bd.squad_attn_flops(*w.geometry())
+    nbytes = bd.squad_attn_bytes(*w.geometry(), dt)
+    t0 = time.perf_counter()
+    q, k, v = wl.device_inputs(w, seed=0)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    sets = [(q, k, v, out)]
+
+    def step(s):
+        bd.squad_attn_fwd(s[0], s[1], s[2], grid, window, out=s[3])
+
+    for _ in range(warmup):
+        step(sets[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(sets[0])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    local_ms = time_loop(lambda s: bd.squad_attn_local(s[0], s[1], s[2], grid, window, out=s[3]), kernel_iters, sets)
+    global_ms = time_loop(lambda s: bd.squad_attn_global(s[0], s[1], s[3], grid, window, out=s[3]),
+                          kernel_iters, sets)
+    rec = {"config": {"B": w.B, "heads": w.heads, "d": w.d, "grid": list(grid), "window": list(window), "n": w.n,
+                      "m": w.m, "n_windows": w.n_windows}, "dtype": w.dtype, "steps": steps, "warmup": warmup,
+           "ms_per_block": ms, "local_pass_ms": local_ms, "global_pass_ms": global_ms}
+    if w.dtype == "bf16":
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rec.update({"effective_tflops": flops / (ms * 1e-3) / 1e12, "algorithmic_gbs": gbs,
+                    "fraction_of_roofline": gbs / HBM_PEAK_GBS,
+                    "local_pass_frac": nbytes / 2 / (local_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "global_pass_frac": nbytes / 2 / (global_ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    eprint(f"[bench] {name}: {ms:.4f} ms/block (local {local_ms:.4f}, global {global_ms:.4f}; "
+           f"inputs generated in {gen_s:.1f} s)")
+    del q, k, v, out, sets
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -320,6 +385,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None, help="workload name (default: the 5B 704p block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the other configurations' figures (other_workloads in the JSON line)")
     ap.add_argument("--kernel-iters", type=int, default=100)
     ap.add_argument("--spin-up-s", type=float, default=0.3,
                     help="untimed steps for this many seconds before the warm-up (GPU clocks to steady state)")
@@ -520,6 +587,11 @@ def main():
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = nbytes
         del src, dst
+    if not args.no_other_workloads and w.name == wl.HEADLINE:
+        del sets, q, k, v
+        torch.cuda.empty_cache()
+        out["other_workloads"] = {name: time_other_workload(name)
+                                  for name in ("tiny_f32", "wan1p3b_480p", "wan5b_4x", "wan14b_4x_cfg")}
     if not args.no_cpu_baseline:
         eprint("[bench] timing the oracle on host cores (bounded sample)")
         out["cpu_baseline"] = cpu_baseline(w)

@@ -63,7 +63,9 @@ def run_bwd(geo, dtype, B=1, heads=2, d=64, seed=0):
 # one block, ragged blocks, several blocks, more query tiles than waves, long
 # windows (m = 336 as the 4x workloads), many windows; local windows of 7, 10
 # and 12 key tiles (m = 100, 150 ragged, 192 whole: the one-sweep local
-# backward on 8 and 12 waves, the latter with every K block of LDS in use)
+# backward on 8 and 12 waves, the latter with every K block of LDS in use);
+# local windows of 15 key tiles (m = 240: the two-sweep kernel with the saved
+# log-sum-exp on 8 waves)
 GEOS = [
     (3, 4, 4, 3, 2, 2),
     (2, 6, 8, 1, 3, 4),
@@ -74,6 +76,7 @@ GEOS = [
     (5, 8, 10, 5, 4, 5),
     (3, 10, 20, 3, 5, 10),
     (3, 8, 16, 3, 8, 8),
+    (3, 8, 20, 3, 8, 10),
 ]
 
 
@@ -120,6 +123,35 @@ def test_backward_headline_sampled_heads():
         do = to_f64(dod[0, :, h, :])
         ref = so.squad_backward_head(q, k, v, do, table)
         check_grads([to_f64(t[0, :, h, :]) for t in (dq, dk, dv)], ref, "bf16", f"wan5b_704p h={h}")
+
+
+@pytest.mark.parametrize("geo", [(3, 4, 4, 3, 2, 2), (3, 8, 16, 3, 8, 8)])
+def test_backward_beyond_one_sweep_row_offsets(geo):
+    # a batch element of n * heads * d >= 2^30 elements: the local pass's backward
+    # leaves the one-sweep kernel (32-bit row offsets) for the two-sweep kernel
+    # with the saved log-sum-exp, on 8 waves (m = 12, one key tile) and on 12
+    # (m = 192, 12 key tiles); sampled heads, first and last included
+    import torch
+    T, Hs, Ws, wt, wh, ww = geo
+    n, d = T * Hs * Ws, 128
+    heads = -(-(1 << 30) // (n * d))
+    assert n * heads * d >= 1 << 30
+    grid, window = (T, Hs, Ws), (wt, wh, ww)
+    log(f"case bwd beyond the one-sweep gate: grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} heads={heads} d={d}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(43)
+    q, k, v, do = (torch.randn(1, n, heads, d, device="cuda", dtype=torch.bfloat16, generator=gen)
+                   for _ in range(4))
+    out = bd.squad_attn_fwd(q, k, v, grid, window)
+    dq, dk, dv = bd.squad_attn_bwd(q, k, v, out, do, grid, window)
+    torch.cuda.synchronize()
+    table = so.window_slot_table(*grid, *window)
+    for h in (0, heads // 2 + 1, heads - 1):
+        qs, ks, vs, ds = (to_f64(x[0, :, h, :]) for x in (q, k, v, do))
+        ref = so.squad_backward_head(qs, ks, vs, ds, table)
+        check_grads([to_f64(t[0, :, h, :]) for t in (dq, dk, dv)], ref, "bf16", f"beyond gate {geo} h={h}")
+    del q, k, v, do, out, dq, dk, dv
+    torch.cuda.empty_cache()
 
 
 def test_backward_deterministic():
@@ -217,7 +249,7 @@ def run_saved(geo, dtype, B=1, heads=2, d=64, seed=0):
     return q, k, v, do, got
 
 
-@pytest.mark.parametrize("geo", [GEOS[0], GEOS[3], GEOS[4]])
+@pytest.mark.parametrize("geo", [GEOS[0], GEOS[3], GEOS[4], GEOS[9]])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_saved_activations_match_recompute(geo, dtype):
     T, Hs, Ws, wt, wh, ww = geo

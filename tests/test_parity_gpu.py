@@ -87,11 +87,13 @@ def test_tiny_geometry_bf16(op):
 # Full-size workloads, sampled heads
 # ---------------------------------------------------------------------------
 
+# every head of the two native blocks; six heads of the 4x blocks, the first
+# and last head of each batch element among them
 SAMPLES = {
-    "wan5b_704p": [(0, 0), (0, 11), (0, 23)],
-    "wan1p3b_480p": [(0, 0), (0, 7)],
-    "wan5b_4x": [(0, 0), (0, 19)],
-    "wan14b_4x_cfg": [(0, 3), (1, 39)],
+    "wan5b_704p": [(0, h) for h in range(24)],
+    "wan1p3b_480p": [(0, h) for h in range(12)],
+    "wan5b_4x": [(0, 0), (0, 5), (0, 11), (0, 16), (0, 19), (0, 23)],
+    "wan14b_4x_cfg": [(0, 0), (0, 17), (0, 39), (1, 0), (1, 22), (1, 39)],
 }
 
 
