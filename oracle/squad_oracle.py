@@ -157,46 +157,6 @@ def squad_attention_reversed(q, k, v, geom):
 
 
 # ---------------------------------------------------------------------------
-# The pages' storage precision
-# ---------------------------------------------------------------------------
-#
-# The pages hold weights and all attention computation in bfloat16 (paperpeel
-# full text, appendix paragraph "Hardware and software environment"): each
-# pass's output -- the local output Y, which the global pass takes as values,
-# and the final O -- is a bfloat16 tensor.  The functions below are the exact
-# passes with exactly those two storage roundings (round to nearest, ties to
-# even) and nothing else rounded: what an exact computation stored at the
-# pages' precision returns.
-
-def round_bf16(x):
-    """Nearest bfloat16 value (8 significant bits, ties to even) of each
-    float64 entry, returned as float64 (normal range; no overflow handling)."""
-    x = np.asarray(x, dtype=np.float64)
-    _, e = np.frexp(x)                  # |x| = f * 2^e with 0.5 <= f < 1
-    ulp = np.ldexp(1.0, e - 8)          # spacing of 8-bit significands in [2^(e-1), 2^e)
-    return np.round(x / ulp) * ulp      # np.round: half to even
-
-
-def squad_head_stored(q, k, v, table):
-    """squad_head with Y and O each rounded to bfloat16."""
-    y = round_bf16(local_pass_head(q, k, v, table))
-    return round_bf16(global_pass_head(q, k, y, table))
-
-
-def local_pass_head_stored(q, k, v, table):
-    return round_bf16(local_pass_head(q, k, v, table))
-
-
-def global_pass_head_stored(q, k, v, table):
-    return round_bf16(global_pass_head(q, k, v, table))
-
-
-def squad_reversed_head_stored(q, k, v, table):
-    y = round_bf16(global_pass_head(q, k, v, table))
-    return round_bf16(local_pass_head(q, k, y, table))
-
-
-# ---------------------------------------------------------------------------
 # Dense n x n form (tiny n only): masks and the effective weight matrix
 # ---------------------------------------------------------------------------
 

@@ -54,22 +54,25 @@ def _record(entry):
             f.write(json.dumps(entry) + "\n")
 
 
-def assert_close_stored(got, exact, stored, what=""):
-    """The bf16 bar at the pages' storage precision.
+def assert_close_bf16_output(got, ref, what=""):
+    """The bf16 bar for outputs stored in bf16 at any magnitude.
 
-    rel-L2 <= 5e-3 against the exact fp64 oracle, and max |got - ref| <= 2e-2
-    against the same oracle with its two stored tensors (the local output Y
-    and the output O) rounded to bf16, as the pages keep all attention
-    computation in bfloat16: at |O| near 4 each of those two roundings alone
-    moves a value by up to 2^-6, so the exact computation stored in bf16 can
-    itself miss the exact oracle by more than 2e-2.
+    rel-L2 <= 5e-3, and max |got - ref| <= 2e-2 plus half the bf16 spacing at
+    |ref|: an output stored in bf16 cannot lie closer to the exact value than
+    that (2^-6 at |ref| in [4, 8), 2^-7 in [2, 4)), and the pages keep all
+    attention computation, so the outputs too, in bfloat16.  Below |ref| = 1
+    the added term is at most 2^-9.
     """
-    max_exact, rel = errors(got, exact)
-    max_abs, _ = errors(got, stored)
-    log(f"  {what}: max_abs={max_abs:.3e} (vs exact {max_exact:.3e}) rel_l2={rel:.3e} max|ref|={np.max(np.abs(exact)):.3f}")
-    _record({"case": what, "dtype": "bf16", "max_abs": max_abs, "max_abs_vs_exact": max_exact, "rel_l2": rel,
-             "max_ref": float(np.max(np.abs(exact))), "stored_precision": True})
-    assert max_abs <= BF16_MAX_ABS and rel <= BF16_REL_L2, (what, max_abs, max_exact, rel)
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    max_abs, rel = errors(got, ref)
+    half = np.ldexp(1.0, np.frexp(np.abs(ref))[1] - 9)
+    excess = float(np.max(np.abs(got - ref) - half)) if got.size else 0.0
+    log(f"  {what}: max_abs={max_abs:.3e} max(|err| - half spacing)={excess:.3e} rel_l2={rel:.3e} "
+        f"max|ref|={np.max(np.abs(ref)):.3f}")
+    _record({"case": what, "dtype": "bf16", "max_abs": max_abs, "max_abs_less_half_spacing": excess,
+             "rel_l2": rel, "max_ref": float(np.max(np.abs(ref)))})
+    assert excess <= BF16_MAX_ABS and rel <= BF16_REL_L2, (what, max_abs, excess, rel)
     return max_abs, rel
 
 

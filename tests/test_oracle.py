@@ -263,56 +263,28 @@ def test_orders_differ_but_both_dense():
     assert np.max(np.abs(W_gl @ v - gl)) < 1e-12
 
 
-# ---- the pages' storage precision (bfloat16 Y and O) -------------------------
+# ---- why the bf16 bar adds half the output's spacing -------------------------
 
-def test_round_bf16_is_round_to_nearest_even():
-    # against torch's float32 -> bfloat16 conversion (round to nearest, ties to
-    # even) on float32-representable values, where no double rounding arises
-    x = np.concatenate([rand(200_000, 91, 3.0), rand(1000, 92, 1e-3), rand(1000, 93, 200.0)])
-    x = x.astype(np.float32).astype(np.float64)
-    lib = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
-    assert np.array_equal(so.round_bf16(x), lib)
-    # hand-worked cases: 8 significant bits, spacing 2^-7 in [1, 2) and 2^-5 in [4, 8)
-    cases = {1 + 2**-8: 1.0, 1 + 3 * 2**-8: 1 + 2**-6, -(1 + 2**-8): -1.0, 1 + 2**-8 + 2**-20: 1 + 2**-7,
-             4 + 2**-6: 4.0, 4 + 3 * 2**-6: 4 + 2**-4, 0.0: 0.0}
-    for a, want in cases.items():
-        assert so.round_bf16(np.array([a]))[0] == want, a
-    # idempotent on its own results
-    r = so.round_bf16(x)
-    assert np.array_equal(so.round_bf16(r), r)
+def _bf16(x):
+    """Round to bfloat16 through torch (round to nearest even) and back to float64."""
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).double().numpy()
 
 
-def test_stored_precision_passes():
-    T, Hs, Ws, wt, wh, ww = TINY
-    n, d = T * Hs * Ws, 16
-    q, k, v = (so.round_bf16(rand((n, d), s)) for s in (94, 95, 96))
-    tab = so.window_slot_table(*TINY)
-    exact = so.squad_head(q, k, v, tab)
-    stored = so.squad_head_stored(q, k, v, tab)
-    # every output is a bfloat16 value
-    assert np.array_equal(so.round_bf16(stored), stored)
-    # error bound: O's own rounding (half its spacing) plus Y's (the global pass
-    # averages Y with weights summing to 1, so Y's rounding errors pass at most
-    # their largest magnitude, half the spacing at max |Y|)
-    y = so.local_pass_head(q, k, v, tab)
-    half = lambda a: np.ldexp(1.0, np.frexp(a)[1] - 9)
-    bound = half(np.abs(exact)) + half(np.max(np.abs(y))) + 1e-12
+def test_bf16_storage_alone_can_exceed_the_plain_absolute_bar():
+    # Head 13 of the headline workload: the exact passes with only their two
+    # stored tensors rounded to bf16 (the local output Y and the output O; the
+    # pages keep all attention computation in bfloat16) already miss the exact
+    # oracle by more than 2e-2, while staying inside 2e-2 plus half the bf16
+    # spacing at |O|, the bar the full-size workload tests use.
+    w = wl.WORKLOADS["wan5b_704p"]
+    table = so.window_slot_table(w.T, w.Hs, w.Ws, w.wt, w.wh, w.ww)
+    q, k, v = wl.head_slices_f64(w, 0, 13)
+    exact = so.squad_head(q, k, v, table)
+    stored = _bf16(so.global_pass_head(q, k, _bf16(so.local_pass_head(q, k, v, table)), table))
     err = np.abs(stored - exact)
-    assert np.all(err <= bound)
-    assert np.max(err) > 0  # the roundings do happen
-    # a constant bfloat16 value passes through both passes unchanged
-    c = np.tile(so.round_bf16(rand((1, d), 97)), (n, 1))
-    assert np.array_equal(so.squad_head_stored(q, k, c, tab), c)
-    # the single passes and the other order, likewise bounded and representable
-    for fn, ex in ((so.local_pass_head_stored, so.local_pass_head),
-                   (so.global_pass_head_stored, so.global_pass_head)):
-        got, want = fn(q, k, v, tab), ex(q, k, v, tab)
-        assert np.all(np.abs(got - want) <= half(np.abs(want)) + 1e-12)
-    rev = so.squad_reversed_head_stored(q, k, v, tab)
-    assert np.array_equal(so.round_bf16(rev), rev)
-    yg = so.global_pass_head(q, k, v, tab)
-    rev_exact = so.squad_reversed_head(q, k, v, tab)
-    assert np.all(np.abs(rev - rev_exact) <= half(np.abs(rev_exact)) + half(np.max(np.abs(yg))) + 1e-12)
+    assert err.max() > 2e-2
+    half_spacing = np.ldexp(1.0, np.frexp(np.abs(exact))[1] - 9)
+    assert np.all(err <= 2e-2 + half_spacing)
 
 
 def test_flop_count_matches_printed_numbers():
