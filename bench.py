@@ -36,11 +36,23 @@ KERNEL_SOURCES = ["sub_quadratic_factorized_amd/csrc/squad_pass_bf16.hip",
                   "sub_quadratic_factorized_amd/csrc/squad_layout.h"]
 # rocprofv3 runs whose CSV output --summarize-profiles turns into the files under profiles/
 PROFILE_ARGS = "--no-cpu-baseline --no-other-workloads --steps 20 --warmup 2 --kernel-iters 20 --copy-calibration-mib 512"
+# counter passes (each within the per-block limits of one rocprofv3 run)
+COUNTER_PASSES = {
+    "mfma_lds": "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_LDS "
+                "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_VALU SQ_BUSY_CYCLES GRBM_GUI_ACTIVE",
+    "waits": "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY "
+             "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM GRBM_GUI_ACTIVE",
+    "rdreq": "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum",
+    "wrreq": "TCC_BUBBLE_sum TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum",
+}
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d <out>/trace -o run -- python3 bench.py " + PROFILE_ARGS,
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d <out>/fetch -o run -- python3 bench.py " + PROFILE_ARGS,
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d <out>/write -o run -- python3 bench.py " + PROFILE_ARGS,
 }
+for _name, _ctrs in COUNTER_PASSES.items():
+    PROFILE_COMMANDS[_name] = (f"rocprofv3 --pmc {_ctrs} -f csv -d <out>/{_name} -o run -- python3 bench.py "
+                               + PROFILE_ARGS)
 PASS_KERNELS = {"squad_local_pass": "squad_local_pass_bf16", "squad_global_pass": "squad_global_pass_bf16"}
 
 
@@ -329,7 +341,7 @@ def cpu_baseline(w, runs=3):
     }
 
 
-def time_other_workload(name, steps=20, warmup=5, kernel_iters=10):
+def time_other_workload(name, steps=20, warmup=5, kernel_iters=10, spin_up_s=0.3):
     """One of the other configurations, timed like the headline (a single
     input set: each of these sets exceeds the last-level cache on its own;
     the tiny fp32 case is launch-bound and reported in ms only)."""
@@ -351,6 +363,13 @@ def time_other_workload(name, steps=20, warmup=5, kernel_iters=10):
     def step(s):
         bd.squad_attn_fwd(s[0], s[1], s[2], grid, window, out=s[3])
 
+    # the GPU idled while the inputs were generated: untimed steps for
+    # spin_up_s bring its clocks back up, then the warm-up
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < spin_up_s:
+        for _ in range(5):
+            step(sets[0])
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step(sets[0])
     torch.cuda.synchronize()

@@ -309,6 +309,26 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         }
     };
 
+    // V operands of a step (instances whose K and V operands are read whole,
+    // OPH == 1): read right after the score MFMAs are issued, before the
+    // softmax, so that their LDS latency hides behind the softmax arithmetic
+    // (a transposing fetch: lane (li, lg) addresses row 4*lg + li/4, and that
+    // +16, at 4 consecutive d: column 4*(dt/2) + li%4, half dt%2; it receives 4
+    // consecutive keys of one d column)
+    bf16x8 vop[G::DT];
+    auto read_v = [&](int buf) {
+        const uint16_t* vb = vbuf[buf];
+        const int vr = v_fetch_row(li, lg);
+#pragma unroll
+        for (int dt = 0; dt < G::DT; ++dt) {
+            const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            vop[dt] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+        }
+    };
+
     // K block: scores of this wave's tiles, online-softmax update, bf16 P.
     auto k_step = [&](int buf, int blk) {
         f32x4 s0[QT], s1[QT];
@@ -340,6 +360,16 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                 }
             }
             if (OPH > 1) __builtin_amdgcn_sched_barrier(0);
+            if (OPH == 1) {
+                // every K operand read ahead of the score MFMAs (one LDS round
+                // trip per step instead of one per pair of MFMAs)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * G::KS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * G::KS * QT, 0);
+            }
+        }
+        if constexpr (OPH == 1) {
+            read_v(buf);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * G::DT, 1);
         }
         const bool mask = ragged && blk == NB - 1;
         const int kbase = blk * BR + 4 * lg;
@@ -383,13 +413,18 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // plus 4) so a lane's 4+4 accumulator rows are 8 consecutive d.
     auto v_step = [&](int buf) {
         uint16_t* vb = vbuf[buf];
-        // transposing fetch: lane (li, lg) addresses row 4*lg + li/4 (and that
-        // +16) at 4 consecutive d (column 4*(dt/2) + li%4, half dt%2); it
-        // receives 4 consecutive keys of one d column
         const int vr = v_fetch_row(li, lg);
 #pragma unroll
         for (int t = 0; t < QT; ++t)
             osum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[t], osum[t], 0, 0, 0);
+        if constexpr (OPH == 1) {  // V operands already read (read_v)
+#pragma unroll
+            for (int t = 0; t < QT; ++t)
+#pragma unroll
+                for (int dt = 0; dt < G::DT; ++dt)
+                    oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pk[t], oacc[t][dt], 0, 0, 0);
+            return;
+        }
         // the V operands in OPH parts, as the K operands above
 #pragma unroll
         for (int h = 0; h < OPH; ++h) {
@@ -592,8 +627,10 @@ int grid_for(const void* kern, int threads, int nprob, int mult) {
 // the waves of one workgroup; a workgroup has at least NCH/64 waves (8 at
 // d = 128, 4 at d = 64) so that every thread stages one chunk per tensor.  The
 // register budget follows the waves that share a SIMD (<= 12 waves: 168
-// VGPRs; 8 waves: 256).  Problems of up to 12 tiles run one tile per wave, of
-// 13-24 tiles 2 or 3 tiles per wave on 8 waves (each key and value read once).
+// VGPRs; 8 waves: 256).  Problems of up to 12 tiles run one tile per wave
+// with two steps in flight (four left fewer registers for the operand reads
+// and ran slower), of 13-24 tiles 2 or 3 tiles per wave on 8 waves (each key
+// and value read once).
 // Longer ones are split into 2 parts of query rows (items) run by the 2-tile
 // instance when the problem count is a multiple of 8 and the pass is not in
 // place (a part writes its rows of `out` while another part of the problem
@@ -647,7 +684,7 @@ hipError_t launch_menu(const PassGeom& g0, const void* q, const void* k, const v
     }
     const int waves = g.part_tiles > minw ? g.part_tiles : minw;
     if (g.parts > 1) return launch_one<D, 2, 8, 4, 2, 256, true, PAD, FAST, true>(g, 8, q, k, v, o, y, lse, st);
-    if (tiles <= 12) return launch_one<D, 1, 12, 4, 3, 192, true, PAD, FAST>(g, waves, q, k, v, o, y, lse, st);
+    if (tiles <= 12) return launch_one<D, 1, 12, 2, 3, 192, true, PAD, FAST>(g, waves, q, k, v, o, y, lse, st);
     if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
     if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
     return launch_one<D, 4, 8, 2, 2, 512, false, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
