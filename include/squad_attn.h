@@ -30,7 +30,8 @@
  * Ownership.  The caller allocates and owns every buffer.  The library keeps no
  * per-call state and allocates nothing; out doubles as the intermediate Y of
  * squad_attn_fwd, so no workspace is needed (the padded entry point takes one
- * for the padded positions).  Prior contents of out are
+ * for the padded positions; its no-allocation variant uses a fixed device
+ * buffer of the library's own instead).  Prior contents of out are
  * ignored; they are undefined after a failed launch.
  *
  * Semantics.  Every compute entry point is asynchronous on `stream` (0 = the
@@ -76,8 +77,12 @@ typedef enum {
     SQUAD_ERR_ALIAS = 4,
     SQUAD_ERR_ALIGN = 5,
     SQUAD_ERR_HIP = 6,
-    SQUAD_ERR_WORKSPACE = 7
+    SQUAD_ERR_WORKSPACE = 7,
+    SQUAD_ERR_SCRATCH = 8
 } squad_status_t;
+
+/* Size of the fixed device scratch of squad_attn_fwd_padded_noalloc. */
+#define SQUAD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* out = Attn_G(q, k, Attn_L(q, k, v)): the SQuad-Attention forward pass.
  * Enqueues the local pass (writing Y into out) and then the global pass
@@ -145,6 +150,33 @@ squad_status_t squad_attn_fwd_padded(const void* q, const void* k, const void* v
                                      int B, int heads, int T, int Hs, int Ws,
                                      int wt, int wh, int ww, int d,
                                      int dtype, hipStream_t stream);
+
+/* squad_attn_fwd_padded for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and the same `out` bit for bit when squad_attn_fwd_padded's
+ * workspace would hold only the padded positions, with no workspace argument.
+ * The padded positions' local outputs go to a fixed scratch buffer of the
+ * library's own, SQUAD_NOALLOC_SCRATCH_BYTES (32 MiB) of device memory that
+ * each device the library runs on holds until the process ends; its address
+ * is looked up once per device, on the first call on it.  The call makes no
+ * allocation (no hipMalloc, no hipFree, no allocating library routine).  The
+ * global pass always runs in place on `out` (no region for Y).
+ *
+ * Every call on one device shares that device's scratch and it keeps the last
+ * call's contents: calls that may overlap in time on one device (different
+ * streams, or different host threads, without ordering between them) race on
+ * it and must not be issued.  Nothing needs to start at zero: the local pass
+ * writes the whole side buffer before the global pass reads it.
+ *
+ * Arguments and errors as squad_attn_fwd_padded without the workspace, except
+ * SQUAD_ERR_SCRATCH (after the NULL checks, before any HIP call) when
+ * B * (padded positions per batch element) * heads * d * sizeof(dtype)
+ * exceeds SQUAD_NOALLOC_SCRATCH_BYTES.  When the window tiles the grid the
+ * call is squad_attn_fwd and uses no scratch. */
+squad_status_t squad_attn_fwd_padded_noalloc(const void* q, const void* k, const void* v, void* out,
+                                             int B, int heads, int T, int Hs, int Ws,
+                                             int wt, int wh, int ww, int d,
+                                             int dtype, hipStream_t stream);
 
 /* Validation only for squad_attn_fwd_padded (pure host function). */
 squad_status_t squad_attn_check_padded(const void* q, const void* k, const void* v, const void* out,
@@ -322,7 +354,8 @@ int squad_attn_last_hip_error(void);
 
 /* Version of this ABI (bumped on any change; 2 adds the padded entry points,
  * the backward and SQUAD_ERR_WORKSPACE; 3 the saved-activation forward and
- * backward, and the padded workspace's region for Y). */
+ * backward, and the padded workspace's region for Y; 4 the padded forward
+ * without allocation and SQUAD_ERR_SCRATCH). */
 int squad_attn_abi_version(void);
 
 #ifdef __cplusplus

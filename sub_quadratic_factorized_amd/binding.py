@@ -28,10 +28,12 @@ SQUAD_ERR_ALIAS = 4
 SQUAD_ERR_ALIGN = 5
 SQUAD_ERR_HIP = 6
 SQUAD_ERR_WORKSPACE = 7
+SQUAD_ERR_SCRATCH = 8
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SQUAD_NOALLOC_SCRATCH_BYTES
 
 COMPUTE_ENTRY_POINTS = ("squad_attn_fwd", "squad_attn_local", "squad_attn_global", "squad_attn_fwd_reversed")
 ALL_SYMBOLS = COMPUTE_ENTRY_POINTS + (
-    "squad_attn_fwd_padded", "squad_attn_check_padded", "squad_attn_padded_workspace_bytes",
+    "squad_attn_fwd_padded", "squad_attn_fwd_padded_noalloc", "squad_attn_check_padded", "squad_attn_padded_workspace_bytes",
     "squad_attn_flops_padded", "squad_attn_bytes_padded", "squad_window_solve",
     "squad_attn_bwd", "squad_attn_check_bwd", "squad_attn_bwd_workspace_bytes", "squad_attn_bwd_flops",
     "squad_attn_bwd_bytes", "squad_attn_fwd_save", "squad_attn_bwd_saved", "squad_attn_bwd_saved_workspace_bytes",
@@ -69,6 +71,8 @@ def lib() -> ctypes.CDLL:
     sz, ip = ctypes.c_size_t, ctypes.POINTER(ctypes.c_int)
     L.squad_attn_fwd_padded.argtypes = [p, p, p, p, p, sz] + [i] * 10 + [p]
     L.squad_attn_fwd_padded.restype = i
+    L.squad_attn_fwd_padded_noalloc.argtypes = [p, p, p, p] + [i] * 10 + [p]
+    L.squad_attn_fwd_padded_noalloc.restype = i
     L.squad_attn_check_padded.argtypes = [p, p, p, p, p, sz] + [i] * 10
     L.squad_attn_check_padded.restype = i
     L.squad_attn_padded_workspace_bytes.argtypes = [i] * 10
@@ -283,6 +287,26 @@ def squad_attn_fwd_padded(q, k, v, grid, window, out=None, workspace=None, strea
                                          stream)
     if st != SQUAD_OK:
         raise SquadError(st, "squad_attn_fwd_padded")
+    return out
+
+
+def squad_attn_fwd_padded_noalloc(q, k, v, grid, window, out=None, stream=None):
+    """squad_attn_fwd_padded without a workspace: the padded positions' local
+    outputs go to the library's fixed device scratch (the C call allocates
+    nothing; pass `out` to keep this wrapper from allocating it).  Calls on one
+    device must not overlap in time."""
+    import torch
+    out = _check_tensors(q, k, v, out, grid)
+    B, n, heads, d = q.shape
+    T, Hs, Ws = grid
+    wt, wh, ww = window
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = lib().squad_attn_fwd_padded_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, heads,
+                                                 T, Hs, Ws, wt, wh, ww, d, _dtype_code(q), stream)
+    if st != SQUAD_OK:
+        raise SquadError(st, "squad_attn_fwd_padded_noalloc")
     return out
 
 

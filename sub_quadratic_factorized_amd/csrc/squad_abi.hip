@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace squad {
 
 namespace {
@@ -149,12 +151,14 @@ PassGeom make_geom(const Problem& pr, bool global);
 // would split its problems were it not in place, Y of every real token after
 // it, so that the local pass writes Y there and the global pass reads its
 // values from there and writes `out` (not in place).
-void padded_workspace(Problem* pr) {
+// With allow_y false (the fixed scratch of the no-allocation entry point) the
+// workspace is the side buffer alone and the global pass runs in place.
+void padded_workspace(Problem* pr, bool allow_y = true) {
     const size_t es = (size_t)esize(pr->dtype);
     const size_t side = (size_t)pr->B * (size_t)pr->npad * (size_t)pr->heads * (size_t)pr->d * es;
     pr->ybuf_off = 0;
     pr->ws_bytes = side;
-    if (pr->npad > 0 && pr->dtype == SQUAD_BF16 && pass_bf16_splits(make_geom(*pr, true))) {
+    if (allow_y && pr->npad > 0 && pr->dtype == SQUAD_BF16 && pass_bf16_splits(make_geom(*pr, true))) {
         pr->ybuf_off = (side + 255) & ~(size_t)255;
         pr->ws_bytes = pr->ybuf_off + (size_t)pr->B * (size_t)pr->n * (size_t)pr->heads * (size_t)pr->d * es;
     }
@@ -165,9 +169,12 @@ void padded_workspace(Problem* pr) {
 // When the window tiles the grid nothing is padded, the workspace is ignored
 // and out == v stays allowed; otherwise out must not overlap v at all (the
 // mirror images of a window's padded rows are other windows' rows of v).
+// fixed_scratch: the workspace is the library's own scratch of ws_size bytes
+// (ws unused): a side buffer larger than it is SQUAD_ERR_SCRATCH, and the
+// workspace's pointer checks do not apply.
 squad_status_t validate_padded(const void* q, const void* k, const void* v, const void* out, const void* ws,
                                size_t ws_size, int B, int heads, int T, int Hs, int Ws, int wt, int wh, int ww,
-                               int d, int dtype, Problem* pr, bool* empty) {
+                               int d, int dtype, Problem* pr, bool* empty, bool fixed_scratch = false) {
     squad_status_t s = check_shape_padded(B, heads, T, Hs, Ws, wt, wh, ww, d, pr, empty);
     if (s != SQUAD_OK) return s;
     if (*empty) return SQUAD_OK;
@@ -179,15 +186,20 @@ squad_status_t validate_padded(const void* q, const void* k, const void* v, cons
     if (padded && (T > kMaxPaddedT || pr->Hp > kMaxPaddedHW || pr->Wp > kMaxPaddedHW)) return SQUAD_ERR_UNSUPPORTED;
     pr->dtype = dtype;
     if (!q || !k || !v || !out) return SQUAD_ERR_NULL;
-    padded_workspace(pr);
-    if (padded && (!ws || ws_size < pr->ws_bytes)) return SQUAD_ERR_WORKSPACE;
+    padded_workspace(pr, !fixed_scratch);
+    if (fixed_scratch) {
+        if (padded && ws_size < pr->ws_bytes) return SQUAD_ERR_SCRATCH;
+    } else if (padded && (!ws || ws_size < pr->ws_bytes)) {
+        return SQUAD_ERR_WORKSPACE;
+    }
+    const bool caller_ws = padded && !fixed_scratch;
     uintptr_t bits = ((uintptr_t)q) | ((uintptr_t)k) | ((uintptr_t)v) | ((uintptr_t)out);
-    if (padded) bits |= (uintptr_t)ws;
+    if (caller_ws) bits |= (uintptr_t)ws;
     if (bits & 15u) return SQUAD_ERR_ALIGN;
     pr->bytes = (size_t)pr->elems * (size_t)esize(dtype);
     if (overlaps(out, q, pr->bytes) || overlaps(out, k, pr->bytes)) return SQUAD_ERR_ALIAS;
     if ((padded || out != v) && overlaps(out, v, pr->bytes)) return SQUAD_ERR_ALIAS;
-    if (padded) {
+    if (caller_ws) {
         const uintptr_t w = (uintptr_t)ws, e = w + pr->ws_bytes;
         for (const void* t : {q, k, v, out}) {
             const uintptr_t a = (uintptr_t)t;
@@ -491,6 +503,41 @@ squad_status_t run(Kind kind, const void* q, const void* k, const void* v, void*
     return hip_status(e);
 }
 
+// ---- fixed scratch of squad_attn_fwd_padded_noalloc ------------------------
+// Device memory of the library's own, so that the entry point allocates
+// nothing: each device the library runs on holds one copy until the process
+// ends.  On the host the name `scratch` is only a stand-in for the symbol, not
+// a device address; the address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[SQUAD_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// This device's scratch address (looked up on the first call on a device), or
+// null with *err set.
+void* scratch_on_current_device(hipError_t* err) {
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        if (ptr == nullptr) {
+            *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 int device_cu_count() {
@@ -545,6 +592,25 @@ squad_status_t squad_attn_fwd_padded(const void* q, const void* k, const void* v
     }
     return squad::hip_status(
         squad::run_two_passes(pr, true, q, k, v, out, pr.npad > 0 ? workspace : nullptr, stream));
+}
+
+squad_status_t squad_attn_fwd_padded_noalloc(const void* q, const void* k, const void* v, void* out, int B, int heads,
+                                             int T, int Hs, int Ws, int wt, int wh, int ww, int d, int dtype,
+                                             hipStream_t stream) {
+    squad::Problem pr;
+    bool empty = false;
+    const squad_status_t s = squad::validate_padded(q, k, v, out, nullptr, SQUAD_NOALLOC_SCRATCH_BYTES, B, heads, T,
+                                                    Hs, Ws, wt, wh, ww, d, dtype, &pr, &empty, true);
+    if (s != SQUAD_OK || empty) return s;
+    void* side = nullptr;
+    if (pr.npad > 0) {
+        hipError_t e = hipSuccess;
+        side = squad::scratch_on_current_device(&e);
+        if (side == nullptr) return squad::hip_status(e);
+    }
+    // the side buffer is written whole by the local pass before the global
+    // pass reads it, so nothing of an earlier call's contents is used
+    return squad::hip_status(squad::run_two_passes(pr, true, q, k, v, out, side, stream));
 }
 
 squad_status_t squad_attn_check_padded(const void* q, const void* k, const void* v, const void* out,
@@ -726,12 +792,15 @@ const char* squad_status_str(int status) {
         case SQUAD_ERR_ALIGN: return "pointer not 16-byte aligned";
         case SQUAD_ERR_HIP: return "HIP runtime or launch error";
         case SQUAD_ERR_WORKSPACE: return "workspace missing or smaller than squad_attn_padded_workspace_bytes";
+        case SQUAD_ERR_SCRATCH:
+            return "the padded positions' local outputs need more than the no-allocation entry point's fixed "
+                   "scratch (SQUAD_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
 
 int squad_attn_last_hip_error(void) { return squad::g_last_hip_error; }
 
-int squad_attn_abi_version(void) { return 3; }
+int squad_attn_abi_version(void) { return 4; }
 
 }  // extern "C"

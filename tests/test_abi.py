@@ -39,7 +39,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert set(bd.ALL_SYMBOLS) == set(names)
     for n in names:
         assert getattr(lib, n) is not None
-    assert lib.squad_attn_abi_version() == 3
+    assert lib.squad_attn_abi_version() == 4
 
 
 def test_exports_via_nm():
@@ -163,7 +163,7 @@ def test_flops_and_bytes_helpers():
 
 
 def test_status_strings():
-    for s in range(8):  # every status the header defines
+    for s in range(9):  # every status the header defines
         assert isinstance(bd.status_str(s), str) and bd.status_str(s)
     assert bd.status_str(123) == "unknown status"
     assert bd.lib().squad_attn_last_hip_error() == 0
@@ -244,6 +244,33 @@ def test_padded_check_accepts_what_would_launch():
     assert pcall(ww=4, ws=0, ws_bytes=0, out=V) == bd.SQUAD_OK
     assert pcall(B=0, q=0, ws=0) == bd.SQUAD_OK
     assert pcall("fwd", B=0, q=0, k=0, v=0, out=0, ws=0) == bd.SQUAD_OK   # empty: nothing enqueued
+
+
+def ncall(q=Q, k=K, v=V, out=O, dtype=bd.SQUAD_BF16, **over):
+    g = dict(PGEO)
+    g.update(over)
+    return bd.lib().squad_attn_fwd_padded_noalloc(q, k, v, out, g["B"], g["heads"], g["T"], g["Hs"], g["Ws"],
+                                                  g["wt"], g["wh"], g["ww"], g["d"], dtype, None)
+
+
+def test_noalloc_rejections_before_any_hip_call():
+    # the padded entry point's checks without a workspace, and the fixed
+    # scratch's limit: 924 padded positions x heads x 128 x 2 bytes fits
+    # 32 MiB up to 141 heads
+    assert bd.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert 924 * 141 * 128 * 2 <= bd.NOALLOC_SCRATCH_BYTES < 924 * 142 * 128 * 2
+    assert ncall(heads=142) == bd.SQUAD_ERR_SCRATCH
+    assert ncall(heads=71, dtype=bd.SQUAD_F32) == bd.SQUAD_ERR_SCRATCH
+    assert ncall(heads=142, q=0) == bd.SQUAD_ERR_NULL           # null before scratch
+    assert ncall(wt=4) == bd.SQUAD_ERR_SHAPE
+    assert ncall(ww=41) == bd.SQUAD_ERR_SHAPE
+    assert ncall(d=96) == bd.SQUAD_ERR_UNSUPPORTED
+    assert ncall(q=0) == bd.SQUAD_ERR_NULL
+    assert ncall(out=O + 8) == bd.SQUAD_ERR_ALIGN
+    assert ncall(out=V) == bd.SQUAD_ERR_ALIAS                   # padded: no in-place over v
+    assert ncall(out=K + 32) == bd.SQUAD_ERR_ALIAS
+    assert ncall(B=0, q=0, k=0, v=0, out=0) == bd.SQUAD_OK      # empty: nothing enqueued
+    assert "scratch" in bd.status_str(bd.SQUAD_ERR_SCRATCH)
 
 
 def test_padded_flops_and_bytes_helpers():
