@@ -121,46 +121,69 @@ def short_kernel_name(name: str) -> str:
     return base + ("<" + targs if targs else "")
 
 
-def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload: str,
-                       trace_log: str | None = None) -> None:
-    """Write profiles/ summaries from the CSV output of the three PROFILE_COMMANDS runs.
+MI355X_XCDS = 8          # GRBM_GUI_ACTIVE in the counter CSV is summed over the XCDs
+MI355X_SIMDS = 256 * 4   # 256 CUs of 4 SIMDs
 
-    Hardware counters are scaled by what they read for the plain 512 MiB
-    device copy the same runs make (its bytes are known), so FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch) become HBM bytes per launch of each pass."""
+
+def _counter_means(d: str):
+    """{(kernel, counter): (mean value per dispatch, dispatches)} of one rocprofv3 --pmc run's CSV."""
+    import csv
+    vals = {}
+    for row in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+        key = (short_kernel_name(row["Kernel_Name"]), row["Counter_Name"])
+        vals.setdefault(key, []).append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
+
+
+def _kernels_with(means, counter):
+    return sorted({k for k, c in means if c == counter})
+
+
+def summarize_profiles(prof_dir: str, workload: str, trace_log: str | None = None) -> None:
+    """Write the profiles/ summaries from one folder holding the CSV output of
+    every PROFILE_COMMANDS run (one subfolder per run, named as its key).
+
+    HBM bytes come from the read and write request counts by size
+    (TCC_EA0_RDREQ_32B/64B/128B, TCC_EA0_WRREQ and _64B) times their sizes, with
+    no fitted factor; FETCH_SIZE and WRITE_SIZE are listed beside them for the
+    plain device copy the same runs make (its bytes are known)."""
     import csv
     from sub_quadratic_factorized_amd import workloads as wl
     w = wl.WORKLOADS[workload]
     esize = 2 if w.dtype == "bf16" else 4
-    pass_bytes = 4 * w.B * w.n * w.heads * w.d * esize
+    tensor = w.B * w.n * w.heads * w.d * esize
+    pass_bytes = 4 * tensor
     copy_bytes = 512 << 20
+    sub = {k: os.path.join(prof_dir, k) for k in PROFILE_COMMANDS}
+    rd, wr = _counter_means(sub["rdreq"]), _counter_means(sub["wrreq"])
+    fetch, write = _counter_means(sub["fetch"]), _counter_means(sub["write"])
+    ml, wt = _counter_means(sub["mfma_lds"]), _counter_means(sub["waits"])
 
-    def counter_means(d, counter):
-        vals = {}
-        for row in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
-            if row["Counter_Name"] != counter:
-                continue
-            vals.setdefault(short_kernel_name(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
-        return {k: (sum(v) / len(v), len(v)) for k, v in vals.items()}
-
-    fetch, write = counter_means(fetch_dir, "FETCH_SIZE"), counter_means(write_dir, "WRITE_SIZE")
-    copy_name = next(k for k in fetch if "copyBuffer" in k)
-    fetch_scale = copy_bytes / 1024 / fetch[copy_name][0]
-    write_scale = copy_bytes / 1024 / write[copy_name][0]
+    def hbm(kernel):
+        g = lambda m, c: m.get((kernel, c), (0.0, 0))[0]
+        n128, n64, n32 = g(rd, "TCC_EA0_RDREQ_128B_sum"), g(rd, "TCC_EA0_RDREQ_64B_sum"), g(rd, "TCC_EA0_RDREQ_32B_sum")
+        nall = g(rd, "TCC_EA0_RDREQ_sum")
+        w64, wall = g(wr, "TCC_EA0_WRREQ_64B_sum"), g(wr, "TCC_EA0_WRREQ_sum")
+        return (128 * n128 + 64 * n64 + 32 * n32, 64 * w64 + 32 * (wall - w64),
+                nall - n128 - n64 - n32, g(wr, "TCC_BUBBLE_sum"))
 
     stats = []
-    for row in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))):
+    for row in csv.DictReader(open(os.path.join(sub["trace"], "run_kernel_stats.csv"))):
         stats.append((short_kernel_name(row["Name"]), int(row["Calls"]), float(row["AverageNs"]) / 1e3,
                       float(row["MinNs"]) / 1e3, float(row["MaxNs"]) / 1e3))
+    avg_us = lambda k: next((s[2] for s in stats if s[0] == k), float("nan"))
     title = (f"{w.name}: B={w.B}, grid {w.T}x{w.Hs}x{w.Ws} (n={w.n}), {w.heads} heads, d={w.d}, "
              f"window {w.wt}x{w.wh}x{w.ww} (m={w.m}, N_w={w.n_windows}), {w.dtype}")
     src_hash = kernel_source_hash()
+    wl_arg = "" if w.name == wl.HEADLINE else f" --workload {w.name}"
+    cmd = lambda k: PROFILE_COMMANDS[k] + wl_arg
+    intro = ("Commands (repository root on one MI355X, `export TMPDIR=/tmp` first; <out> any scratch folder; "
+             "each counter pass is a run of its own):\n\n```\n")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"kernel_trace_squad_passes_{w.name}.md"), "w") as f:
-        f.write(f"# Kernel trace: SQuad-Attention passes, {title}\n\n")
-        f.write("Command (repository root on one MI355X, after `cd /tmp && export TMPDIR=/tmp`; <out> any "
-                "scratch folder; --workload omitted = this workload):\n\n")
-        f.write("```\n" + PROFILE_COMMANDS["trace"] + "\n```\n\n")
+    out = lambda name: open(os.path.join(ROOT, "profiles", f"{name}_{w.name}.md"), "w")
+
+    with out("kernel_trace_squad_passes") as f:
+        f.write(f"# Kernel trace: SQuad-Attention passes, {title}\n\n" + intro + cmd("trace") + "\n```\n\n")
         f.write(f"Kernel source hash (bench.py kernel_source_hash): {src_hash}\n\n")
         f.write("| kernel | calls | average (us) | min (us) | max (us) |\n|---|---|---|---|---|\n")
         for name, calls, avg, lo, hi in stats:
@@ -170,70 +193,107 @@ def summarize_profiles(trace_dir: str, fetch_dir: str, write_dir: str, workload:
             own = [ln.strip() for ln in open(trace_log) if ln.startswith("[bench] ") and " ms" in ln]
             f.write("\nbench.py's own HIP-event timings in the same profiled process (stderr):\n\n```\n"
                     + "\n".join(own) + "\n```\n")
-    lines = []
-    for kname, kernel in PASS_KERNELS.items():
-        fk = next(k for k in fetch if k.startswith(kernel))
-        wk = next(k for k in write if k.startswith(kernel))
-        rd = fetch[fk][0] * fetch_scale * 1024
-        wr = write[wk][0] * write_scale * 1024
-        avg_us = next(s[2] for s in stats if s[0].startswith(kernel))
-        rec = {
-            "kernel": kname, "instance": fk, "workload": w.name,
-            "fetch_size_kib_per_dispatch": fetch[fk][0], "write_size_kib_per_dispatch": write[wk][0],
-            "dispatches": [fetch[fk][1], write[wk][1]],
-            "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_scale": fetch_scale, "write_scale": write_scale},
-            "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
-            "hbm_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": pass_bytes,
-            "kernel_source_hash": src_hash,
-            "commands": [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"]],
-        }
+
+    copy = next(k for k, c in rd if c == "TCC_EA0_RDREQ_sum" and "copyBuffer" in k)
+    c_rd, c_wr, c_other, c_bubble = hbm(copy)
+    c_fetch = fetch.get((copy, "FETCH_SIZE"), (0.0, 0))[0] * 1024
+    c_write = write.get((copy, "WRITE_SIZE"), (0.0, 0))[0] * 1024
+    rows, brows = [], []
+    for kname, prefix in PASS_KERNELS.items():
+        kern = next(k for k in _kernels_with(rd, "TCC_EA0_RDREQ_sum") if k.startswith(prefix))
+        r, wbytes, _, _ = hbm(kern)
+        rec = {"kernel": kname, "instance": kern, "workload": w.name,
+               "hbm_read_bytes_per_launch": r, "hbm_write_bytes_per_launch": wbytes,
+               "hbm_bytes_per_launch": r + wbytes, "algorithmic_bytes_per_launch": pass_bytes,
+               "method": "read requests x their sizes (TCC_EA0_RDREQ_128B/64B/32B) + write requests x "
+                         "their sizes (TCC_EA0_WRREQ, _64B), mean per dispatch",
+               "kernel_source_hash": src_hash, "commands": [cmd("rdreq"), cmd("wrreq")]}
         with open(os.path.join(ROOT, "profiles", f"traffic_{kname}_{w.name}.json"), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
-        lines.append(f"| {fk} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} | {pass_bytes / 1e6:.1f} | "
-                     f"{(rd + wr) / pass_bytes:.3f} | {avg_us:.1f} | {(rd + wr) / avg_us / 1e3:.0f} |")
-    with open(os.path.join(ROOT, "profiles", f"hbm_traffic_squad_passes_{w.name}.md"), "w") as f:
-        f.write(f"# HBM traffic per launch: SQuad-Attention passes, {title}\n\n")
-        f.write("Commands (two counter passes, each its own run; repository root, after "
-                "`cd /tmp && export TMPDIR=/tmp`):\n\n```\n" + PROFILE_COMMANDS["fetch"] + "\n"
-                + PROFILE_COMMANDS["write"] + "\n```\n\n")
-        f.write(f"Kernel source hash: {src_hash}\n\n")
-        f.write(f"Calibration: the same runs copy {copy_bytes >> 20} MiB device to device ({copy_name}); "
-                f"FETCH_SIZE reads {fetch[copy_name][0]:.0f} KiB and WRITE_SIZE {write[copy_name][0]:.0f} KiB "
-                f"for it, so the scale factors are {fetch_scale:.3f} (reads) and {write_scale:.3f} (writes).\n\n")
-        f.write("| kernel | HBM read (MB) | HBM write (MB) | total (MB) | algorithmic (MB) | ratio | "
-                "trace avg (us) | GB/s |\n|---|---|---|---|---|---|---|---|\n")
-        f.write("\n".join(lines) + "\n")
-    # the backward's two kernels (the same runs time squad_attn_bwd and squad_attn_bwd_saved):
-    # algorithmic bytes in tensor-sizes T = B*n*heads*d elements, per-row arrays not counted --
-    # the global pass's backward reads q, k, Y, O, dO and writes dY and its dq, dk contributions
-    # (8 T); the local pass's reads q, k, v, dY and those contributions and writes dq, dk, dv (9 T)
-    tensor = w.B * w.n * w.heads * w.d * esize
-    blines = []
-    for kernel, alg, what in (("squad_bwd_pass_bf16<128, false", 8 * tensor, "global pass"),
+        t = avg_us(kern)
+        rows.append(f"| {kern} | {r / 1e6:.1f} | {wbytes / 1e6:.1f} | {(r + wbytes) / 1e6:.1f} | "
+                    f"{pass_bytes / 1e6:.1f} | {(r + wbytes) / pass_bytes:.3f} | {t:.1f} | "
+                    f"{(r + wbytes) / t / 1e3:.0f} |")
+    # the backward's kernels: the global pass's backward reads q, k, Y, O, dO and writes dY and its dq,
+    # dk contributions (8 tensor-sizes); the local pass's reads q, k, v, dY and those contributions
+    # and writes dq, dk, dv (9); per-row float32 arrays not counted
+    for prefix, alg, what in (("squad_bwd_pass_bf16<128, false", 8 * tensor, "global pass"),
+                              ("squad_bwd_onesweep_global_bf16<128", 8 * tensor, "global pass, one sweep"),
                               ("squad_bwd_onesweep_bf16<128", 9 * tensor, "local pass, one sweep"),
                               ("squad_bwd_pass_bf16<128, true", 9 * tensor, "local pass")):
-        fk = next((k for k in fetch if k.startswith(kernel)), None)
-        wk = next((k for k in write if k.startswith(kernel)), None)
-        st = next((s for s in stats if s[0].startswith(kernel)), None)
-        if fk is None or wk is None or st is None:
+        kern = next((k for k in _kernels_with(rd, "TCC_EA0_RDREQ_sum") if k.startswith(prefix)), None)
+        if kern is None:
             continue
-        rd = fetch[fk][0] * fetch_scale * 1024
-        wr = write[wk][0] * write_scale * 1024
-        blines.append(f"| {fk} ({what}) | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} | "
-                      f"{alg / 1e6:.1f} | {(rd + wr) / alg:.3f} | {st[2]:.1f} | {(rd + wr) / st[2] / 1e3:.0f} |")
-    if blines:
-        with open(os.path.join(ROOT, "profiles", f"hbm_traffic_squad_backward_{w.name}.md"), "w") as f:
-            f.write(f"# HBM traffic per launch: SQuad-Attention backward kernels, {title}\n\n")
-            f.write("From the same two counter runs as the passes' summary (the runs time squad_attn_bwd "
-                    "and squad_attn_bwd_saved after the forward), scaled the same way:\n\n```\n"
-                    + PROFILE_COMMANDS["fetch"] + "\n" + PROFILE_COMMANDS["write"] + "\n```\n\n")
+        r, wbytes, _, _ = hbm(kern)
+        t = avg_us(kern)
+        brows.append(f"| {kern} ({what}) | {r / 1e6:.1f} | {wbytes / 1e6:.1f} | {(r + wbytes) / 1e6:.1f} | "
+                     f"{alg / 1e6:.1f} | {(r + wbytes) / alg:.3f} | {t:.1f} | {(r + wbytes) / t / 1e3:.0f} |")
+    head = ("| kernel | HBM read (MB) | HBM write (MB) | total (MB) | algorithmic (MB) | ratio | "
+            "trace avg (us) | GB/s |\n|---|---|---|---|---|---|---|---|\n")
+    with out("hbm_traffic_squad_passes") as f:
+        f.write(f"# HBM traffic per launch: SQuad-Attention passes, {title}\n\n" + intro + cmd("rdreq") + "\n"
+                + cmd("wrreq") + "\n" + cmd("fetch") + "\n" + cmd("write") + "\n" + cmd("trace") + "\n```\n\n")
+        f.write(f"Kernel source hash: {src_hash}\n\n")
+        f.write("Bytes = read requests times their sizes (TCC_EA0_RDREQ_128B, _64B, _32B) plus write requests "
+                "times theirs (TCC_EA0_WRREQ, of which _64B), mean per dispatch; no scale factor.\n\n")
+        f.write(f"Cross-check on the plain {copy_bytes >> 20} MiB device copy of the same runs ({copy}): "
+                f"requests read {c_rd / 2**20:.1f} MiB and write {c_wr / 2**20:.1f} MiB "
+                f"({c_other:.0f} read requests of other sizes). FETCH_SIZE reads {c_fetch / 2**20:.1f} MiB and "
+                f"WRITE_SIZE {c_write / 2**20:.1f} MiB for it: FETCH_SIZE's expression counts 128-byte reads "
+                f"through TCC_BUBBLE (here {c_bubble:.0f}) and every other non-32-byte read as 64 bytes, so on "
+                f"this part, where reads go out as 128-byte requests and TCC_BUBBLE stays 0, it reports half "
+                f"the bytes read.\n\n")
+        f.write(head + "\n".join(rows) + "\n")
+    if brows:
+        with out("hbm_traffic_squad_backward") as f:
+            f.write(f"# HBM traffic per launch: SQuad-Attention backward kernels, {title}\n\n"
+                    "From the same counter runs as the passes' summary (the runs time squad_attn_bwd and "
+                    "squad_attn_bwd_saved after the forward), bytes from request counts by size:\n\n```\n"
+                    + cmd("rdreq") + "\n" + cmd("wrreq") + "\n```\n\n")
             f.write("Algorithmic bytes: the global pass's backward reads q, k, Y, O and dO and writes dY and "
                     "its dq, dk contributions (8 tensor-sizes); the local pass's reads q, k, v, dY and those "
                     "contributions and writes dq, dk, dv (9); per-row float32 arrays not counted.\n\n")
-            f.write("| kernel | HBM read (MB) | HBM write (MB) | total (MB) | algorithmic (MB) | ratio | "
-                    "trace avg (us) | GB/s |\n|---|---|---|---|---|---|---|---|\n")
-            f.write("\n".join(blines) + "\n")
+            f.write(head + "\n".join(brows) + "\n")
+
+    # MFMA, LDS and wave states per kernel
+    mrows = []
+    flops_alg = {"squad_local_pass": 4 * w.B * w.heads * w.d * w.n * w.m,
+                 "squad_global_pass": 4 * w.B * w.heads * w.d * w.n * w.n_windows}
+    kernels = [k for k in _kernels_with(ml, "SQ_INSTS_VALU_MFMA_MOPS_BF16") if "squad" in k]
+    for kern in kernels:
+        g = lambda m, c: m.get((kern, c), (0.0, 0))[0]
+        cyc = g(ml, "GRBM_GUI_ACTIVE") / MI355X_XCDS
+        busy = g(ml, "SQ_VALU_MFMA_BUSY_CYCLES") / max(cyc * MI355X_SIMDS, 1.0)
+        flops = g(ml, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+        t = avg_us(kern)
+        lds_active = g(ml, "SQ_LDS_IDX_ACTIVE")
+        conflict = g(ml, "SQ_LDS_BANK_CONFLICT") / lds_active if lds_active else 0.0
+        wave = g(wt, "SQ_WAVE_CYCLES")
+        frac = lambda c: g(wt, c) / wave if wave else 0.0
+        alg = next((v for k2, v in flops_alg.items() if kern.startswith(PASS_KERNELS[k2])), None)
+        mrows.append(
+            f"| {kern} | {t:.1f} | {flops / 1e9:.2f} | {'' if alg is None else f'{alg / 1e9:.2f}'} | "
+            f"{flops / t / 1e6:.0f} | {100 * busy:.1f} | {g(ml, 'SQ_INSTS_MFMA') / 1e6:.2f} | "
+            f"{g(ml, 'SQ_INSTS_VALU') / 1e6:.2f} | {g(ml, 'SQ_INSTS_LDS') / 1e6:.2f} | {100 * conflict:.1f} | "
+            f"{100 * frac('SQ_ACTIVE_INST_ANY'):.0f} | {100 * frac('SQ_WAIT_INST_ANY'):.0f} | "
+            f"{100 * frac('SQ_WAIT_ANY'):.0f} | {100 * frac('SQ_WAIT_INST_LDS'):.0f} |")
+    with out("mfma_lds_squad_passes") as f:
+        f.write(f"# MFMA, LDS and wave states per launch: SQuad-Attention kernels, {title}\n\n" + intro
+                + cmd("mfma_lds") + "\n" + cmd("waits") + "\n" + cmd("trace") + "\n```\n\n")
+        f.write(f"Kernel source hash: {src_hash}\n\n")
+        f.write("Per dispatch, mean over the runs' dispatches. MFMA FLOPs = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 "
+                "(the work the MFMAs did, padded tiles and the row-sum MFMA included); algorithmic = "
+                "4 B h d n L of the pass. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x "
+                f"{MI355X_SIMDS} SIMDs). Instruction counts are wave instructions (millions). LDS conflict = "
+                "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. Wave states are shares of SQ_WAVE_CYCLES: "
+                "issuing (SQ_ACTIVE_INST_ANY), waiting to issue (SQ_WAIT_INST_ANY), waiting on a counter "
+                "(SQ_WAIT_ANY, s_waitcnt and barriers), of which for LDS (SQ_WAIT_INST_LDS). MFMA peak: "
+                f"{BF16_MFMA_PEAK_TFLOPS:.0f} TFLOP/s dense bf16.\n\n")
+        f.write("| kernel | trace avg (us) | MFMA GFLOP | algorithmic GFLOP | MFMA TFLOP/s | MFMA busy % | "
+                "MFMA instr (M) | VALU instr (M) | LDS instr (M) | LDS conflict % | active % | wait-issue % | "
+                "wait-counter % | wait LDS % |\n|---|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+        f.write("\n".join(mrows) + "\n")
 
 
 # Backbones of the FLOP-conformance sweep: native latent grid (81 frames, T = 21)
@@ -411,7 +471,7 @@ def main():
                     help="untimed steps for this many seconds before the warm-up (GPU clocks to steady state)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling hardware byte counters)")
-    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--summarize-profiles", metavar="PROF_DIR",
                     help="write the profiles/ summaries from rocprofv3 CSV output, then exit (no GPU needed)")
     ap.add_argument("--trace-log", default=None, help="stderr of the profiled trace run (with --summarize-profiles)")
     ap.add_argument("--sweep", action="store_true",
@@ -420,7 +480,7 @@ def main():
 
     if args.summarize_profiles:
         from sub_quadratic_factorized_amd import workloads as wl
-        summarize_profiles(*args.summarize_profiles, args.workload or wl.HEADLINE, args.trace_log)
+        summarize_profiles(args.summarize_profiles, args.workload or wl.HEADLINE, args.trace_log)
         return
 
     if args.gpus != 1:
