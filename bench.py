@@ -239,7 +239,7 @@ def summarize_profiles(prof_dir: str, workload: str, trace_log: str | None = Non
                 "times theirs (TCC_EA0_WRREQ, of which _64B), mean per dispatch; no scale factor.\n\n")
         f.write(f"Cross-check on the plain {copy_bytes >> 20} MiB device copy of the same runs ({copy}): "
                 f"requests read {c_rd / 2**20:.1f} MiB and write {c_wr / 2**20:.1f} MiB "
-                f"({c_other:.0f} read requests of other sizes). FETCH_SIZE reads {c_fetch / 2**20:.1f} MiB and "
+                f"({int(round(c_other))} read requests of other sizes). FETCH_SIZE reads {c_fetch / 2**20:.1f} MiB and "
                 f"WRITE_SIZE {c_write / 2**20:.1f} MiB for it: FETCH_SIZE's expression counts 128-byte reads "
                 f"through TCC_BUBBLE (here {c_bubble:.0f}) and every other non-32-byte read as 64 bytes, so on "
                 f"this part, where reads go out as 128-byte requests and TCC_BUBBLE stays 0, it reports half "
