@@ -8,8 +8,10 @@
 //
 // Workgroup organisation
 //   * Persistent: a workgroup walks work items blockIdx.x, +gridDim.x, ...: a
-//     whole problem, or (problems of more than 24 query tiles, in a pass that
-//     is not in place) one of the 2 parts of its query rows.  A whole problem is owned by one
+//     whole problem, or for problems of more than 24 query tiles one of the 2
+//     parts of its query rows (a pass that is not in place) or one of the 2
+//     halves of its value columns (in place: each half reads and writes only
+//     its own columns of the value rows).  An item is owned by one
 //     workgroup, which reads all of its rows before it writes any (this is
 //     what makes the in-place global pass safe).
 //   * The work of an item is NB = ceil(L/32) steps.  Step b brings in 32 rows
@@ -68,7 +70,7 @@ using Geo = BlockGeo<D>;
 // through buffer descriptors based at a problem's base row, so a chunk's
 // address is a single 32-bit offset, and loads of dead steps return zeros
 // without a memory access.
-template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT, bool FAST>
+template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT, bool FAST, bool DH>
 __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __restrict__ qp,
                                           const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
                                           uint16_t* yp, float* lse_out, float scale_log2) {
@@ -118,17 +120,28 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // (b, h) offsets into the tensors
     // and into the side buffer, and the packed base coordinates; and its query
     // rows q0 .. q0 + qn - 1 of the problem.
+    // DH: items are (problem, half of d) pairs; dh is the half whose P V
+    // columns the item computes, reads and writes (0 when !DH)
     struct Prob {
         int64_t off, yoff;
-        int base, q0, qn;
+        int base, q0, qn, dh;
     };
     auto problem = [&](int it) -> Prob {
-        int p = (int)blockIdx.x + it * (int)gridDim.x, part = 0;
+        int p = (int)blockIdx.x + it * (int)gridDim.x, part = 0, dh = 0;
         if (SPLIT) {  // item 8 (c * parts + part) + x -> problem 8 c + x
             const int y = p >> 3;
             const int c = (int)fdiv((uint32_t)y, g.div_parts);
             part = y - c * g.parts;
             p = c * 8 + (p & 7);
+        }
+        if (DH) {  // item 8 (2 c + half) + x -> problem 8 c + x, or item 2 p + half
+            if (g.nprob % 8 == 0) {
+                dh = (p >> 3) & 1;
+                p = ((p >> 4) << 3) + (p & 7);
+            } else {
+                dh = p & 1;
+                p >>= 1;
+            }
         }
         const int q0 = SPLIT ? part * g.part_tiles * 16 : 0;
         const int qn = SPLIT ? min(L - q0, g.part_tiles * 16) : L;
@@ -136,9 +149,9 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         if (PAD)
             return Prob{(int64_t)pr.b * g.n * row_stride + (int64_t)pr.h * D,
                         (int64_t)pr.b * g.npad * row_stride + (int64_t)pr.h * D,
-                        GP ? slot_coords(g, pr.pi) : win_coords(g, pr.pi), q0, qn};
+                        GP ? slot_coords(g, pr.pi) : win_coords(g, pr.pi), q0, qn, dh};
         const int base = GP ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
-        return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0, q0, qn};
+        return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0, q0, qn, dh};
     };
     // offset, in q, k and the local pass's values, of the row with table entry tv
     auto src_off = [&](const Prob& pr, uint32_t tv) -> int64_t {
@@ -170,8 +183,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // FAST: a descriptor without records, which returns zeros)
     bool ld_dead = nmine <= 0;
     bool q_dead = nmine <= 1;
-    Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0, 0, 1};
-    Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0, 0, 1};
+    Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0, 0, 1, 0};
+    Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0, 0, 1, 0};
 
     // FAST: descriptors of the loader's problems, and this thread's row
     // offsets for the next call (read one call ahead)
@@ -189,7 +202,10 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     auto issue_fast = [&](u32x4& dk, u32x4& dv, u32x4& dq) {
         const uint32_t o = nk_off + col_bytes;
         dk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-        dv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+        // DH: V chunks outside the item's half read the problem's first chunk
+        // (one cached line; never used)
+        const bool vhalf = !DH || ((ld_col >= D / 2) == (ld_p.dh != 0));
+        dv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vhalf ? o : 0u, 0, 0));
         if (QSTAGE) {
             if (SPLIT)
                 dq = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -227,7 +243,9 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             av = ld_p.yoff + (int64_t)pad_index(g, ld_p.base + (int)tv) * row_stride + ld_col;
         }
         dk = *reinterpret_cast<const u32x4*>(kp + (ld_dead ? 0 : a));
-        dv = *reinterpret_cast<const u32x4*>(vb + (ld_dead ? 0 : av));
+        // DH: V chunks outside the item's half read the tensor's first 16 bytes
+        const bool vhalf = !DH || ((ld_col >= D / 2) == (ld_p.dh != 0));
+        dv = *reinterpret_cast<const u32x4*>(vb + (ld_dead || !vhalf ? 0 : av));
         if (QSTAGE) {
             // row of the next item's query rows (unsplit: the key / value row)
             const uint32_t tq = SPLIT ? tab[ld_q.q0 + min(ld_b * BR + ld_row, ld_q.qn - 1)] : tv;
@@ -262,7 +280,9 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 
     // ---- per-wave compute state --------------------------------------------
     bf16x8 qreg[QT][G::KS];
-    f32x4 oacc[QT][G::DT];
+    // output d-tiles held: all, or (DH) the item's half, d-tiles dt0 .. dt0 + NDT - 1
+    constexpr int NDT = DH ? G::DT / 2 : G::DT;
+    f32x4 oacc[QT][NDT];
     f32x4 osum[QT];  // every row: running sum of P for the lane's query
     bf16x8 pk[QT];
     float mrun[QT];
@@ -280,7 +300,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // Q tiles of this wave (from the LDS stage, or straight from memory) into
     // MFMA B-operand registers
     auto read_q = [&]() {
-        const Prob qprob = QSTAGE ? Prob{0, 0, 0, 0, 1} : problem(c_it);
+        const Prob qprob = QSTAGE ? Prob{0, 0, 0, 0, 1, 0} : problem(c_it);
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             const int row = (wave * QT + t) * 16 + li;
@@ -305,7 +325,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             mrun[t] = -INFINITY;
             osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dt = 0; dt < G::DT; ++dt) oacc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int dt = 0; dt < NDT; ++dt) oacc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
 
@@ -315,17 +335,19 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // (a transposing fetch: lane (li, lg) addresses row 4*lg + li/4, and that
     // +16, at 4 consecutive d: column 4*(dt/2) + li%4, half dt%2; it receives 4
     // consecutive keys of one d column)
-    bf16x8 vop[G::DT];
+    bf16x8 vop[NDT];
     auto read_v = [&](int buf) {
         const uint16_t* vb = vbuf[buf];
         const int vr = v_fetch_row(li, lg);
+        const int dt0 = DH ? cur_p.dh * NDT : 0;
 #pragma unroll
-        for (int dt = 0; dt < G::DT; ++dt) {
+        for (int j = 0; j < NDT; ++j) {
+            const int dt = dt0 + j;
             const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
             const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            vop[dt] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+            vop[j] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
         }
     };
 
@@ -369,7 +391,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         }
         if constexpr (OPH == 1) {
             read_v(buf);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * G::DT, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
         }
         const bool mask = ragged && blk == NB - 1;
         const int kbase = blk * BR + 4 * lg;
@@ -393,7 +415,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                     const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
                     osum[t] *= alpha;
 #pragma unroll
-                    for (int dt = 0; dt < G::DT; ++dt) oacc[t][dt] *= alpha;
+                    for (int dt = 0; dt < NDT; ++dt) oacc[t][dt] *= alpha;
                     mrun[t] = mnew;
                 }
                 const float nm = -mrun[t];
@@ -421,18 +443,19 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 #pragma unroll
             for (int t = 0; t < QT; ++t)
 #pragma unroll
-                for (int dt = 0; dt < G::DT; ++dt)
+                for (int dt = 0; dt < NDT; ++dt)
                     oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pk[t], oacc[t][dt], 0, 0, 0);
             return;
         }
         // the V operands in OPH parts, as the K operands above
+        const int dt0 = DH ? cur_p.dh * NDT : 0;
 #pragma unroll
         for (int h = 0; h < OPH; ++h) {
-            constexpr int ND = G::DT / OPH;
+            constexpr int ND = NDT / OPH;
             bf16x8 va[ND];
 #pragma unroll
             for (int i = 0; i < ND; ++i) {
-                const int dt = h * ND + i;
+                const int dt = dt0 + h * ND + i;
                 const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
@@ -464,15 +487,16 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                 if (keep) {
                     const uint32_t tv = tab[cur_p.q0 + row];
 #pragma unroll
-                    for (int p = 0; p < D / 32; ++p) {
+                    for (int p = 0; p < NDT / 2; ++p) {
                         bf16x8 o;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             o[i] = static_cast<__bf16>(oacc[t][2 * p][i] * inv);
                             o[4 + i] = static_cast<__bf16>(oacc[t][2 * p + 1][i] * inv);
                         }
+                        const uint32_t pp = (uint32_t)(p + (DH ? cur_p.dh * NDT / 2 : 0));
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro,
-                                                               tv + 16u * lg + 64u * p, 0, 0);
+                                                               tv + 16u * lg + 64u * pp, 0, 0);
                     }
                     // optional row log-sum-exp (log2 units, scores scaled by
                     // log2(e)/sqrt(d)), [B, n, heads] float32
@@ -495,14 +519,15 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             }
             if (keep) {
 #pragma unroll
-                for (int p = 0; p < D / 32; ++p) {
+                for (int p = 0; p < NDT / 2; ++p) {
                     bf16x8 o;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         o[i] = static_cast<__bf16>(oacc[t][2 * p][i] * inv);
                         o[4 + i] = static_cast<__bf16>(oacc[t][2 * p + 1][i] * inv);
                     }
-                    *reinterpret_cast<bf16x8*>(dst + 32 * p) = o;
+                    const int pp = p + (DH ? cur_p.dh * NDT / 2 : 0);
+                    *reinterpret_cast<bf16x8*>(dst + 32 * pp) = o;
                 }
                 // optional row log-sum-exp (log2 units, scores scaled by
                 // log2(e)/sqrt(d)) of unpadded grids, [B, n, heads] float32
@@ -566,18 +591,19 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 }
 
 // The two passes as distinct kernels (so profiles tell them apart).
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT, bool FAST>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT, bool FAST,
+          bool DH = false>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_local_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float* lse_out, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT, FAST>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT, FAST, DH>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT, bool DH = false>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_global_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float* lse_out, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT, false>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT, false, DH>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
 // Workgroups for a persistent launch over nprob items, a multiple of `mult`
@@ -638,25 +664,37 @@ int grid_for(const void* kern, int threads, int nprob, int mult) {
 // 8 items apart and the grid is a multiple of 8 * parts, so they run in the
 // same round on workgroups 8 apart, which round-robin dispatch puts on the
 // same XCD, and their repeated key / value reads are mostly served by its L2.
-// Otherwise 4 tiles go on each wave (whose registers spill).  The unpadded local pass takes
+// Otherwise (in place, or a problem count not a multiple of 8) each problem
+// becomes 2 items, one per half of the value columns (d), each computing all
+// of the problem's scores with 4 query tiles per wave: the half-width output
+// accumulators leave room for the four tiles' queries (no scratch; all four
+// tiles' full-width accumulators spilled about 490 bytes per lane, 1.6 TB/s
+// for a forward with a 408-window global pass, against 2.3 TB/s now, where
+// splitting by query rows reaches 3 TB/s but cannot run in place).  The
+// unpadded local pass takes
 // the FAST loader when a batch element of a tensor spans less than 4 GiB.
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool FAST, bool SPLIT = false>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool FAST, bool SPLIT = false,
+          bool DH = false>
 hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o, void* y,
                       float* lse, hipStream_t st) {
     using KernelFn = void (*)(PassGeom, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, uint16_t*,
                               float*, float);
     KernelFn kfn;
     if constexpr (FAST)
-        kfn = &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, true>;
+        kfn = &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, true, DH>;
     else
-        kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT>
-                       : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, false>;
+        kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, DH>
+                       : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, false, DH>;
     const void* kern = reinterpret_cast<const void*>(kfn);
     const int threads = 64 * waves;
     if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.part_tiles * 16 > LMAX || g.part_tiles > QT * waves ||
-        (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0) || (FAST && (g.global || !fast_ok<D>(g))))
+        (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0) || (g.dsplit != 0) != DH ||
+        (DH && (SPLIT || g.nitems != 2 * g.nprob)) || (FAST && (g.global || !fast_ok<D>(g))))
         return hipErrorInvalidConfiguration;  // the menu never asks for this
-    const int grid = grid_for(kern, threads, g.nitems, g.parts > 1 ? 8 * g.parts : 1);
+    // split items of one problem run in the same round: query parts 8 apart,
+    // d halves 8 apart (or adjacent when nprob % 8 != 0)
+    const int mult = g.parts > 1 ? 8 * g.parts : DH ? (g.nprob % 8 == 0 ? 16 : 2) : 1;
+    const int grid = grid_for(kern, threads, g.nitems, mult);
     const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf((float)D);
     hipLaunchKernelGGL(kfn, dim3(grid), dim3(threads), 0, st, g, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o),
@@ -687,7 +725,12 @@ hipError_t launch_menu(const PassGeom& g0, const void* q, const void* k, const v
     if (tiles <= 12) return launch_one<D, 1, 12, 2, 3, 192, true, PAD, FAST>(g, waves, q, k, v, o, y, lse, st);
     if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
     if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
-    return launch_one<D, 4, 8, 2, 2, 512, false, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
+    // not split into query parts (in place, or a problem count not a multiple
+    // of 8): each problem becomes two items, one per half of d, 4 query tiles
+    // per wave (Q straight from memory: L = 512 does not fit an LDS stage)
+    g.dsplit = 1;
+    g.nitems = 2 * g.nprob;
+    return launch_one<D, 4, 8, 2, 2, 512, false, PAD, FAST, false, true>(g, 8, q, k, v, o, y, lse, st);
 }
 
 template <int D, bool PAD>

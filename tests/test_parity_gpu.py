@@ -298,10 +298,15 @@ def test_split_many_slots_global():
 
 @pytest.mark.parametrize("fn", ["local", "global", "fwd", "reversed"])
 def test_in_place_long_problems_against_oracle(fn):
-    # lengths that split when not in place (m = 336 local, N_w = 400 global,
-    # problem counts multiples of 8): in place every pass must stay whole
+    # lengths that split into query parts when not in place (m = 336 local,
+    # N_w = 400 global, problem counts multiples of 8): in place a pass is
+    # never split by query rows; problems of 25-32 query tiles are split by
+    # halves of d instead (N_w = 400 and 500 global, m = 400 local; the halves
+    # of a problem 8 items apart, or adjacent for 6 problems), at d = 64 and 128
     import torch
-    for geo, heads, d in (((21, 8, 8, 21, 4, 4), 8, 64), ((2, 20, 80, 1, 2, 4), 2, 64)):
+    for geo, heads, d in (((21, 8, 8, 21, 4, 4), 8, 64), ((2, 20, 80, 1, 2, 4), 2, 64),
+                          ((2, 20, 80, 1, 2, 4), 2, 128), ((2, 20, 75, 1, 2, 3), 1, 128),
+                          ((1, 20, 40, 1, 20, 20), 2, 128)):
         T, Hs, Ws, wt, wh, ww = geo
         log(f"case in-place {fn} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} heads={heads}")
         q, k, v = wl.random_geometry_inputs(1, heads, T * Hs * Ws, d, "bf16", seed=23)
