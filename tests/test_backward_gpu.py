@@ -65,7 +65,9 @@ def run_bwd(geo, dtype, B=1, heads=2, d=64, seed=0):
 # and 12 key tiles (m = 100, 150 ragged, 192 whole: the one-sweep local
 # backward on 8 and 12 waves, the latter with every K block of LDS in use);
 # local windows of 15 key tiles (m = 240: the two-sweep kernel with the saved
-# log-sum-exp on 8 waves)
+# log-sum-exp on 8 waves); global passes of 110 (7 key tiles, ragged, as the
+# headline's) and 128 windows (8 whole tiles) over single-token and two-token
+# windows
 GEOS = [
     (3, 4, 4, 3, 2, 2),
     (2, 6, 8, 1, 3, 4),
@@ -77,6 +79,8 @@ GEOS = [
     (3, 10, 20, 3, 5, 10),
     (3, 8, 16, 3, 8, 8),
     (3, 8, 20, 3, 8, 10),
+    (1, 10, 22, 1, 1, 2),
+    (1, 8, 16, 1, 1, 1),
 ]
 
 
