@@ -286,6 +286,10 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     f32x4 osum[QT];  // every row: running sum of P for the lane's query
     bf16x8 pk[QT];
     float mrun[QT];
+    // mrun + kRescaleHeadroom, kept for instances of up to two tiles per wave
+    // (the 3- and 4-tile ones have no registers to spare and add it per block)
+    constexpr bool KEEP_THR = QT <= 2;
+    float mthr[KEEP_THR ? QT : 1];
     Prob cur_p{0, 0, 0, 0, 1};
     __amdgpu_buffer_rsrc_t ro;
     if constexpr (FAST) ro = rsrc(op, cur_p, false);
@@ -323,6 +327,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             mrun[t] = -INFINITY;
+            if (KEEP_THR) mthr[KEEP_THR ? t : 0] = -INFINITY;
             osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) oacc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -350,6 +355,13 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             vop[j] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
         }
     };
+
+    // max(a, b) of finite or -inf scores as med3(a, b, big) with big above any
+    // score (|score| <= d * 448^2 in bf16 at d <= 128); big passes through an
+    // empty asm statement so that the compiler cannot fold it into fmaxf
+    float big = 3.0e38f;
+    asm volatile("" : "+s"(big));
+    auto max2 = [&](float a, float b) { return __builtin_amdgcn_fmed3f(a, b, big); };
 
     // K block: scores of this wave's tiles, online-softmax update, bf16 P.
     auto k_step = [&](int buf, int blk) {
@@ -405,18 +417,23 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                         if (kbase + 16 + i >= L) s1[t][i] = -INFINITY;
                     }
                 }
-                float mx = fmaxf(fmaxf(fmaxf(s0[t][0], s0[t][1]), fmaxf(s0[t][2], s0[t][3])),
-                                 fmaxf(fmaxf(s1[t][0], s1[t][1]), fmaxf(s1[t][2], s1[t][3])));
+                // the block maximum of the lane's 8 keys: med3 against a bound
+                // above every score is the maximum, without the operand
+                // canonicalisation fmaxf would add on MFMA results
+                const float mx = max2(max2(max2(s0[t][0], s0[t][1]), max2(s0[t][2], s0[t][3])),
+                                      max2(max2(s1[t][0], s1[t][1]), max2(s1[t][2], s1[t][3])));
                 // a lane's own keys decide whether the row needs a new running
                 // maximum (exactly when the row's keys do); only then is the
                 // maximum reduced across the row's four lanes
-                if (__builtin_amdgcn_ballot_w64(mx * scale_log2 > mrun[t] + kRescaleHeadroom) != 0) {
+                const float thr = KEEP_THR ? mthr[KEEP_THR ? t : 0] : mrun[t] + kRescaleHeadroom;
+                if (__builtin_amdgcn_ballot_w64(mx * scale_log2 > thr) != 0) {
                     const float mnew = fmaxf(mrun[t], row_max4(mx) * scale_log2);
                     const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
                     osum[t] *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) oacc[t][dt] *= alpha;
                     mrun[t] = mnew;
+                    if (KEEP_THR) mthr[KEEP_THR ? t : 0] = mnew + kRescaleHeadroom;
                 }
                 const float nm = -mrun[t];
                 bf16x8 pv;
