@@ -65,6 +65,27 @@ def test_noalloc_float32_and_tiling_window():
     assert torch.equal(out, ref)
 
 
+def test_noalloc_long_global_pass_in_place():
+    # 2x20x79 padded to 2x20x80 with 1x2x4 windows: a 400-window global pass,
+    # which the workspace entry point splits into query parts (Y in its
+    # workspace) and the no-allocation one runs in place as d-half items; both
+    # within the bar of the oracle and of each other
+    import torch
+    for d in (64, 128):
+        B, heads, grid, window = 1, 2, (2, 20, 79), (1, 2, 4)
+        T, Hs, Ws = grid
+        n = T * Hs * Ws
+        log(f"case noalloc long global pass d={d}")
+        q, k, v = wl.random_geometry_inputs(B, heads, n, d, "bf16", seed=75 + d)
+        qd, kd, vd = host_to_device((q, k, v), "bf16")
+        ref_out = bd.squad_attn_fwd_padded(qd, kd, vd, grid, window)
+        out = bd.squad_attn_fwd_padded_noalloc(qd, kd, vd, grid, window, out=torch.full_like(qd, float("nan")))
+        torch.cuda.synchronize()
+        ref = so.squad_attention_padded(q, k, v, (B, heads, T, Hs, Ws, *window, d))
+        assert_close(to_f64(out), ref, "bf16", f"noalloc long global d={d}")
+        assert_close(to_f64(out), to_f64(ref_out), "bf16", f"noalloc vs workspace entry d={d}")
+
+
 def test_noalloc_rejects_shapes_beyond_the_scratch():
     # 924 padded positions x 142 heads x 128 x 2 bytes > 32 MiB: refused before any launch
     import torch
