@@ -229,7 +229,6 @@ PassGeom make_geom(const Problem& pr, bool global) {
     g.part_tiles = (g.L + 15) / 16;
     g.nitems = g.nprob;
     g.div_parts = make_fastdiv(1);
-    g.dsplit = 0;
     g.pad = padded ? 1 : 0;
     g.Hp = Hp;
     g.Wp = Wp;

@@ -71,13 +71,6 @@ struct PassGeom {
     // has parts = 1.
     int parts, part_tiles, nitems;
     FastDiv div_parts;
-    // In-place passes of long problems may instead be split by halves of d:
-    // dsplit = 1 makes every problem 2 items (nitems = 2 * nprob), each
-    // computing all of the problem's scores and softmax but only its half of
-    // the P V columns, reading and writing only that half of the value rows
-    // (so an in-place update stays race-free).  Items of one problem are 8
-    // apart when nprob % 8 == 0, else adjacent.
-    int dsplit;
     int pad;
     int Hp, Wp;
     int pad_per_frame;  // Hs*(Wp - Ws) + (Hp - Hs)*Wp padded tokens per frame

@@ -8,13 +8,15 @@
 //
 // Workgroup organisation
 //   * Persistent: a workgroup walks work items blockIdx.x, +gridDim.x, ...: a
-//     whole problem, or for problems of more than 24 query tiles one of the 2
-//     parts of its query rows (a pass that is not in place) or one of the 2
-//     halves of its value columns (in place: each half reads and writes only
-//     its own columns of the value rows).  An item is owned by one
-//     workgroup, which reads all of its rows before it writes any (this is
-//     what makes the in-place global pass safe).
-//   * The work of an item is NB = ceil(L/32) steps.  Step b brings in 32 rows
+//     whole problem, or for problems of more than 24 query tiles in a pass
+//     that is not in place one of the 2 parts of its query rows.  An item is
+//     owned by one workgroup, which reads all of its rows before it writes
+//     any (this is what makes the in-place global pass safe).  Problems of
+//     more than 24 tiles that are not split take their query rows in two
+//     parts one after the other, the first part keeping every value row in
+//     LDS for the second, so no value row is read from memory after the first
+//     part's outputs are written.
+//   * The work of an item is NB = ceil(L/32) steps (per query part).  Step b brings in 32 rows
 //     of K and of V (block b of this problem) and 32 rows of Q (block b of the
 //     NEXT item's query rows).  Every thread stages one 16-byte chunk of each in
 //     registers, PD steps ahead of use: ~PD * 3 * 32 * D * 2 bytes per
@@ -69,8 +71,15 @@ using Geo = BlockGeo<D>;
 // batch elements span less than 4 GiB per tensor): loads and stores go
 // through buffer descriptors based at a problem's base row, so a chunk's
 // address is a single 32-bit offset, and loads of dead steps return zeros
-// without a memory access.
-template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT, bool FAST, bool DH>
+// without a memory access.  VRES (resident values; whole problems of up to
+// 2 * QT * 16 * waves rows, Q straight from memory): an item is a problem
+// whose query rows are taken in parts of QT * 16 * waves rows one after the
+// other, each part a pass over all key blocks; the first part stores every
+// value block in its own LDS slot and the later parts read them there, their
+// value loads dead.  All value rows are in LDS before the first part's
+// outputs are written, so the in-place global pass stays safe, and each
+// value row is read from memory once.
+template <int D, int QT, int PD, int LMAX, bool QSTAGE, bool GP, bool PAD, bool SPLIT, bool FAST, bool VRES>
 __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __restrict__ qp,
                                           const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
                                           uint16_t* yp, float* lse_out, float scale_log2) {
@@ -79,7 +88,9 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     static_assert(PD % 2 == 0, "the LDS buffer of a step must be known at compile time");
     constexpr int QROWS = QSTAGE ? (LMAX + BR - 1) / BR * BR : 1;
     __shared__ __attribute__((aligned(16))) uint16_t kbuf[2][BR * G::KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t vbuf[2][BR * G::VSTR];
+    static_assert(!VRES || (!QSTAGE && !SPLIT), "resident values: whole problems, Q straight from memory");
+    constexpr int VBUFS = VRES ? (LMAX + BR - 1) / BR : 2;
+    __shared__ __attribute__((aligned(16))) uint16_t vbuf[VBUFS][BR * G::VSTR];
     __shared__ __attribute__((aligned(16))) uint16_t qstage[QROWS * G::KSTR];
     __shared__ uint32_t tab[kMaxLen];
 
@@ -93,7 +104,10 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // rows of the Q stage filled per item (all of a problem's, or of a part's)
     constexpr int QCAP = QSTAGE ? (LMAX + BR - 1) / BR * BR : 0;
     const int nmine = (g.nitems - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int total = nmine * NB;  // steps
+    // VRES: query parts of prow rows, one after another
+    const int prow = VRES ? QT * 16 * (int)(blockDim.x >> 6) : L;
+    const int vparts = VRES ? (L + prow - 1) / prow : 1;
+    const int total = nmine * NB * vparts;  // steps
     const int row_stride = g.heads * D;
     const bool ragged = NB * BR != L;
     // this thread's chunk of every block: row ld_row of the block, 16-byte column ld_col
@@ -120,28 +134,17 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // (b, h) offsets into the tensors
     // and into the side buffer, and the packed base coordinates; and its query
     // rows q0 .. q0 + qn - 1 of the problem.
-    // DH: items are (problem, half of d) pairs; dh is the half whose P V
-    // columns the item computes, reads and writes (0 when !DH)
     struct Prob {
         int64_t off, yoff;
-        int base, q0, qn, dh;
+        int base, q0, qn;
     };
     auto problem = [&](int it) -> Prob {
-        int p = (int)blockIdx.x + it * (int)gridDim.x, part = 0, dh = 0;
+        int p = (int)blockIdx.x + it * (int)gridDim.x, part = 0;
         if (SPLIT) {  // item 8 (c * parts + part) + x -> problem 8 c + x
             const int y = p >> 3;
             const int c = (int)fdiv((uint32_t)y, g.div_parts);
             part = y - c * g.parts;
             p = c * 8 + (p & 7);
-        }
-        if (DH) {  // item 8 (2 c + half) + x -> problem 8 c + x, or item 2 p + half
-            if (g.nprob % 8 == 0) {
-                dh = (p >> 3) & 1;
-                p = ((p >> 4) << 3) + (p & 7);
-            } else {
-                dh = p & 1;
-                p >>= 1;
-            }
         }
         const int q0 = SPLIT ? part * g.part_tiles * 16 : 0;
         const int qn = SPLIT ? min(L - q0, g.part_tiles * 16) : L;
@@ -149,9 +152,9 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         if (PAD)
             return Prob{(int64_t)pr.b * g.n * row_stride + (int64_t)pr.h * D,
                         (int64_t)pr.b * g.npad * row_stride + (int64_t)pr.h * D,
-                        GP ? slot_coords(g, pr.pi) : win_coords(g, pr.pi), q0, qn, dh};
+                        GP ? slot_coords(g, pr.pi) : win_coords(g, pr.pi), q0, qn};
         const int base = GP ? slot_offset(g, pr.pi) : win_origin(g, pr.pi);
-        return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0, q0, qn, dh};
+        return Prob{((int64_t)pr.b * g.n + base) * row_stride + (int64_t)pr.h * D, 0, 0, q0, qn};
     };
     // offset, in q, k and the local pass's values, of the row with table entry tv
     auto src_off = [&](const Prob& pr, uint32_t tv) -> int64_t {
@@ -177,14 +180,14 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // outputs never stored); Q blocks past an item's query rows read a dead
     // address.
     u32x4 sk[PD], sv[PD], sq[PD];
-    int ld_it = 0, ld_b = 0;
+    int ld_it = 0, ld_b = 0, ld_part = 0;
     // loads of steps past the last problem, and of Q past the last problem,
     // all read the first 16 bytes of the tensor (one cached line, never used;
     // FAST: a descriptor without records, which returns zeros)
     bool ld_dead = nmine <= 0;
     bool q_dead = nmine <= 1;
-    Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0, 0, 1, 0};
-    Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0, 0, 1, 0};
+    Prob ld_p = nmine > 0 ? problem(0) : Prob{0, 0, 0, 0, 1};
+    Prob ld_q = nmine > 1 ? problem(1) : Prob{0, 0, 0, 0, 1};
 
     // FAST: descriptors of the loader's problems, and this thread's row
     // offsets for the next call (read one call ahead)
@@ -199,13 +202,26 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
         nk_off = tab[ld_row];
         if (SPLIT) nq_off = tab[ld_q.q0 + min(ld_row, ld_q.qn - 1)];
     }
+    // the loader's next step: the next key block, the next query part of the
+    // same problem (VRES), or the first block of the next item (true)
+    auto advance = [&]() -> bool {
+        if (++ld_b < NB) return false;
+        ld_b = 0;
+        if (VRES && ++ld_part < vparts) return false;
+        ld_part = 0;
+        ++ld_it;
+        ld_dead = ld_it >= nmine;
+        q_dead = ld_it + 1 >= nmine;
+        ld_p = ld_q;
+        if (!q_dead) ld_q = problem(ld_it + 1);
+        return true;
+    };
     auto issue_fast = [&](u32x4& dk, u32x4& dv, u32x4& dq) {
         const uint32_t o = nk_off + col_bytes;
         dk = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-        // DH: V chunks outside the item's half read the problem's first chunk
-        // (one cached line; never used)
-        const bool vhalf = !DH || ((ld_col >= D / 2) == (ld_p.dh != 0));
-        dv = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vhalf ? o : 0u, 0, 0));
+        // VRES: value loads past the first query part return zeros unread
+        dv = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(VRES && ld_part > 0 ? rdead : rv, o, 0, 0));
         if (QSTAGE) {
             if (SPLIT)
                 dq = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -213,13 +229,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             else
                 dq = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0));
         }
-        if (++ld_b == NB) {
-            ld_b = 0;
-            ++ld_it;
-            ld_dead = ld_it >= nmine;
-            q_dead = ld_it + 1 >= nmine;
-            ld_p = ld_q;
-            if (!q_dead) ld_q = problem(ld_it + 1);
+        if (advance()) {
             rk = rsrc(kp, ld_p, !ld_dead);
             rv = rsrc(vp, ld_p, !ld_dead);
             rq = rsrc(qp, ld_q, !q_dead);
@@ -243,23 +253,16 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             av = ld_p.yoff + (int64_t)pad_index(g, ld_p.base + (int)tv) * row_stride + ld_col;
         }
         dk = *reinterpret_cast<const u32x4*>(kp + (ld_dead ? 0 : a));
-        // DH: V chunks outside the item's half read the tensor's first 16 bytes
-        const bool vhalf = !DH || ((ld_col >= D / 2) == (ld_p.dh != 0));
-        dv = *reinterpret_cast<const u32x4*>(vb + (ld_dead || !vhalf ? 0 : av));
+        // VRES: value loads past the first query part read the tensor's first
+        // 16 bytes (one cached line; never used)
+        dv = *reinterpret_cast<const u32x4*>(vb + (ld_dead || (VRES && ld_part > 0) ? 0 : av));
         if (QSTAGE) {
             // row of the next item's query rows (unsplit: the key / value row)
             const uint32_t tq = SPLIT ? tab[ld_q.q0 + min(ld_b * BR + ld_row, ld_q.qn - 1)] : tv;
             const bool qd = q_dead || (SPLIT && ld_b * BR >= ld_q.qn);
             dq = *reinterpret_cast<const u32x4*>(qp + (qd ? 0 : src_off(ld_q, tq) + ld_col));
         }
-        if (++ld_b == NB) {
-            ld_b = 0;
-            ++ld_it;
-            ld_dead = ld_it >= nmine;
-            q_dead = ld_it + 1 >= nmine;
-            ld_p = ld_q;
-            if (!q_dead) ld_q = problem(ld_it + 1);
-        }
+        advance();
     };
 
     // swizzled position of this thread's V chunk (16-byte aligned); its two
@@ -268,11 +271,15 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     const bool v_swap = v_halves_swapped<D>(ld_row);
     const int v_lo = v_put + (v_swap ? 4 : 0), v_hi = v_put + (v_swap ? 0 : 4);
 
-    auto put = [&](const u32x4& dk, const u32x4& dv, const u32x4& dq, int buf, int blk) {
+    // VRES: value block blk goes to its own slot, in the first query part only
+    auto put = [&](const u32x4& dk, const u32x4& dv, const u32x4& dq, int buf, int blk, int part) {
         if (stager) {
             *reinterpret_cast<u32x4*>(&kbuf[buf][ld_row * G::KSTR + ld_col]) = dk;
-            *reinterpret_cast<u32x2*>(&vbuf[buf][v_lo]) = u32x2{dv.x, dv.y};
-            *reinterpret_cast<u32x2*>(&vbuf[buf][v_hi]) = u32x2{dv.z, dv.w};
+            if (!VRES || part == 0) {
+                uint16_t* vd = vbuf[VRES ? blk : buf];
+                *reinterpret_cast<u32x2*>(&vd[v_lo]) = u32x2{dv.x, dv.y};
+                *reinterpret_cast<u32x2*>(&vd[v_hi]) = u32x2{dv.z, dv.w};
+            }
             if (QSTAGE && (!SPLIT || blk * BR < QCAP))
                 *reinterpret_cast<u32x4*>(&qstage[(blk * BR + ld_row) * G::KSTR + ld_col]) = dq;
         }
@@ -280,9 +287,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 
     // ---- per-wave compute state --------------------------------------------
     bf16x8 qreg[QT][G::KS];
-    // output d-tiles held: all, or (DH) the item's half, d-tiles dt0 .. dt0 + NDT - 1
-    constexpr int NDT = DH ? G::DT / 2 : G::DT;
-    f32x4 oacc[QT][NDT];
+    f32x4 oacc[QT][G::DT];
     f32x4 osum[QT];  // every row: running sum of P for the lane's query
     bf16x8 pk[QT];
     float mrun[QT];
@@ -293,7 +298,16 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     Prob cur_p{0, 0, 0, 0, 1};
     __amdgpu_buffer_rsrc_t ro;
     if constexpr (FAST) ro = rsrc(op, cur_p, false);
-    int c_it = 0;
+    int c_it = 0, c_part = 0;
+    // the rows of query part `part` of item `it` (VRES), else the item's
+    auto item_prob = [&](int it, int part) -> Prob {
+        Prob p = problem(it);
+        if (VRES) {
+            p.q0 = part * prow;
+            p.qn = min(L - p.q0, prow);
+        }
+        return p;
+    };
     // waves past the item's last query tile only stage data; a wave's partial
     // tiles compute on clamped rows and are never stored (unsplit: the same
     // for every item)
@@ -304,7 +318,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // Q tiles of this wave (from the LDS stage, or straight from memory) into
     // MFMA B-operand registers
     auto read_q = [&]() {
-        const Prob qprob = QSTAGE ? Prob{0, 0, 0, 0, 1, 0} : problem(c_it);
+        const Prob qprob = QSTAGE ? Prob{0, 0, 0, 0, 1} : item_prob(c_it, c_part);
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             const int row = (wave * QT + t) * 16 + li;
@@ -321,16 +335,16 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     };
 
     auto start_problem = [&]() {
-        cur_p = problem(c_it);
+        cur_p = item_prob(c_it, c_part);
         if constexpr (FAST) ro = rsrc(op, cur_p, true);
-        if (SPLIT) computes = wave * QT * 16 < cur_p.qn;
+        if (SPLIT || VRES) computes = wave * QT * 16 < cur_p.qn;
 #pragma unroll
         for (int t = 0; t < QT; ++t) {
             mrun[t] = -INFINITY;
             if (KEEP_THR) mthr[KEEP_THR ? t : 0] = -INFINITY;
             osum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int dt = 0; dt < G::DT; ++dt) oacc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
 
@@ -340,19 +354,17 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // (a transposing fetch: lane (li, lg) addresses row 4*lg + li/4, and that
     // +16, at 4 consecutive d: column 4*(dt/2) + li%4, half dt%2; it receives 4
     // consecutive keys of one d column)
-    bf16x8 vop[NDT];
+    bf16x8 vop[G::DT];
     auto read_v = [&](int buf) {
         const uint16_t* vb = vbuf[buf];
         const int vr = v_fetch_row(li, lg);
-        const int dt0 = DH ? cur_p.dh * NDT : 0;
 #pragma unroll
-        for (int j = 0; j < NDT; ++j) {
-            const int dt = dt0 + j;
+        for (int dt = 0; dt < G::DT; ++dt) {
             const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
             const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-            vop[j] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+            vop[dt] = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
         }
     };
 
@@ -402,8 +414,8 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             }
         }
         if constexpr (OPH == 1) {
-            read_v(buf);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDT, 1);
+            read_v(VRES ? blk : buf);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * G::DT, 1);
         }
         const bool mask = ragged && blk == NB - 1;
         const int kbase = blk * BR + 4 * lg;
@@ -431,7 +443,7 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                     const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mnew);
                     osum[t] *= alpha;
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) oacc[t][dt] *= alpha;
+                    for (int dt = 0; dt < G::DT; ++dt) oacc[t][dt] *= alpha;
                     mrun[t] = mnew;
                     if (KEEP_THR) mthr[KEEP_THR ? t : 0] = mnew + kRescaleHeadroom;
                 }
@@ -460,19 +472,18 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 #pragma unroll
             for (int t = 0; t < QT; ++t)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
+                for (int dt = 0; dt < G::DT; ++dt)
                     oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[dt], pk[t], oacc[t][dt], 0, 0, 0);
             return;
         }
         // the V operands in OPH parts, as the K operands above
-        const int dt0 = DH ? cur_p.dh * NDT : 0;
 #pragma unroll
         for (int h = 0; h < OPH; ++h) {
-            constexpr int ND = NDT / OPH;
+            constexpr int ND = G::DT / OPH;
             bf16x8 va[ND];
 #pragma unroll
             for (int i = 0; i < ND; ++i) {
-                const int dt = dt0 + h * ND + i;
+                const int dt = h * ND + i;
                 const int off = v_half_offset<D>(vr, v_fetch_col(li, dt), v_fetch_half(dt));
                 const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off]));
                 const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(&vb[off + 16 * G::VSTR]));
@@ -504,16 +515,15 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                 if (keep) {
                     const uint32_t tv = tab[cur_p.q0 + row];
 #pragma unroll
-                    for (int p = 0; p < NDT / 2; ++p) {
+                    for (int p = 0; p < G::DT / 2; ++p) {
                         bf16x8 o;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             o[i] = static_cast<__bf16>(oacc[t][2 * p][i] * inv);
                             o[4 + i] = static_cast<__bf16>(oacc[t][2 * p + 1][i] * inv);
                         }
-                        const uint32_t pp = (uint32_t)(p + (DH ? cur_p.dh * NDT / 2 : 0));
                         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), ro,
-                                                               tv + 16u * lg + 64u * pp, 0, 0);
+                                                               tv + 16u * lg + 64u * (uint32_t)p, 0, 0);
                     }
                     // optional row log-sum-exp (log2 units, scores scaled by
                     // log2(e)/sqrt(d)), [B, n, heads] float32
@@ -536,15 +546,14 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
             }
             if (keep) {
 #pragma unroll
-                for (int p = 0; p < NDT / 2; ++p) {
+                for (int p = 0; p < G::DT / 2; ++p) {
                     bf16x8 o;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         o[i] = static_cast<__bf16>(oacc[t][2 * p][i] * inv);
                         o[4 + i] = static_cast<__bf16>(oacc[t][2 * p + 1][i] * inv);
                     }
-                    const int pp = p + (DH ? cur_p.dh * NDT / 2 : 0);
-                    *reinterpret_cast<bf16x8*>(dst + 32 * pp) = o;
+                    *reinterpret_cast<bf16x8*>(dst + 32 * p) = o;
                 }
                 // optional row log-sum-exp (log2 units, scores scaled by
                 // log2(e)/sqrt(d)) of unpadded grids, [B, n, heads] float32
@@ -575,6 +584,9 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
     // buffer e%2 and the Q stage, issue the loads of step e+PD, one barrier,
     // then the K and V work.  The K/V buffer written at step e was last read at
     // step e-2, which every wave finished before passing the barrier of step e-1.
+    // (VRES: value slot b is written at step b of a problem's first part and
+    // was last read by the previous problem's last part, at least NB steps
+    // earlier; the problem's last part ends with the last value read.)
     // The loop runs whole groups of PD steps.  Loads and LDS stores happen on
     // every step, past the end too (clamped addresses, never consumed), so on
     // every path the staged loads are in issue order (slot 0 oldest) and each
@@ -589,18 +601,21 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
                 start_problem();
                 __syncthreads();
             }
-            put(sk[u], sv[u], sq[u], u & 1, blk);
+            put(sk[u], sv[u], sq[u], u & 1, blk, c_part);
             issue(sk[u], sv[u], sq[u]);
             __syncthreads();
             if (live) {
                 if (computes) {
                     k_step(u & 1, blk);
-                    v_step(u & 1);
+                    v_step(VRES ? blk : (u & 1));
                 }
                 if (++blk == NB) {
                     if (computes) finish_problem();
                     blk = 0;
-                    ++c_it;
+                    if (!VRES || ++c_part == vparts) {
+                        c_part = 0;
+                        ++c_it;
+                    }
                 }
             }
         }
@@ -609,18 +624,18 @@ __device__ __forceinline__ void pass_body(const PassGeom& g, const uint16_t* __r
 
 // The two passes as distinct kernels (so profiles tell them apart).
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT, bool FAST,
-          bool DH = false>
+          bool VRES = false>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_local_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float* lse_out, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT, FAST, DH>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, false, PAD, SPLIT, FAST, VRES>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
-template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT, bool DH = false>
+template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool SPLIT, bool VRES = false>
 __global__ __launch_bounds__(64 * MAXW) __attribute__((amdgpu_waves_per_eu(WPE))) void squad_global_pass_bf16(
     PassGeom g, const uint16_t* __restrict__ qp, const uint16_t* __restrict__ kp, const uint16_t* vp, uint16_t* op,
     uint16_t* yp, float* lse_out, float scale_log2) {
-    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT, false, DH>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
+    pass_body<D, QT, PD, LMAX, QSTAGE, true, PAD, SPLIT, false, VRES>(g, qp, kp, vp, op, yp, lse_out, scale_log2);
 }
 
 // Workgroups for a persistent launch over nprob items, a multiple of `mult`
@@ -681,36 +696,38 @@ int grid_for(const void* kern, int threads, int nprob, int mult) {
 // 8 items apart and the grid is a multiple of 8 * parts, so they run in the
 // same round on workgroups 8 apart, which round-robin dispatch puts on the
 // same XCD, and their repeated key / value reads are mostly served by its L2.
-// Otherwise (in place, or a problem count not a multiple of 8) each problem
-// becomes 2 items, one per half of the value columns (d), each computing all
-// of the problem's scores with 4 query tiles per wave: the half-width output
-// accumulators leave room for the four tiles' queries (no scratch; all four
-// tiles' full-width accumulators spilled about 490 bytes per lane, 1.6 TB/s
-// for a forward with a 408-window global pass, against 2.3 TB/s now, where
-// splitting by query rows reaches 3 TB/s but cannot run in place).  The
-// unpadded local pass takes
-// the FAST loader when a batch element of a tensor spans less than 4 GiB.
+// Otherwise (in place, or a problem count not a multiple of 8) a workgroup
+// takes a whole problem and its two query parts one after the other on the
+// same 2-tile layout, keeping every value row in LDS from the first part
+// (128 KB at L = 512, d = 128), so the second part reads only keys and
+// queries from memory and the update stays in place.  With 24 heads on
+// 21x68x120 and 21x4x5 windows the in-place 408-window global pass takes
+// 1.46 ms this way, against 2.10 ms as two d-half items that each computed
+// all scores, and 1.40 ms split into query parts out of place, which stays
+// the choice where it applies.  The unpadded local pass takes the FAST
+// loader when a batch element of a tensor spans less than 4 GiB.
 template <int D, int QT, int MAXW, int PD, int WPE, int LMAX, bool QSTAGE, bool PAD, bool FAST, bool SPLIT = false,
-          bool DH = false>
+          bool VRES = false>
 hipError_t launch_one(const PassGeom& g, int waves, const void* q, const void* k, const void* v, void* o, void* y,
                       float* lse, hipStream_t st) {
     using KernelFn = void (*)(PassGeom, const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, uint16_t*,
                               float*, float);
     KernelFn kfn;
     if constexpr (FAST)
-        kfn = &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, true, DH>;
+        kfn = &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, true, VRES>;
     else
-        kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, DH>
-                       : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, false, DH>;
+        kfn = g.global ? &squad_global_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, VRES>
+                       : &squad_local_pass_bf16<D, QT, MAXW, PD, WPE, LMAX, QSTAGE, PAD, SPLIT, false, VRES>;
     const void* kern = reinterpret_cast<const void*>(kfn);
     const int threads = 64 * waves;
-    if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.part_tiles * 16 > LMAX || g.part_tiles > QT * waves ||
-        (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0) || (g.dsplit != 0) != DH ||
-        (DH && (SPLIT || g.nitems != 2 * g.nprob)) || (FAST && (g.global || !fast_ok<D>(g))))
+    // resident values: at most two query parts of QT * 16 * waves rows
+    const int tiles_max = VRES ? 2 * QT * waves : QT * waves;
+    if (waves * 64 < Geo<D>::NCH || waves > MAXW || g.part_tiles * 16 > LMAX || g.part_tiles > tiles_max ||
+        (g.parts > 1) != SPLIT || (SPLIT && g.nprob % 8 != 0) || (VRES && g.nitems != g.nprob) ||
+        (FAST && (g.global || !fast_ok<D>(g))))
         return hipErrorInvalidConfiguration;  // the menu never asks for this
-    // split items of one problem run in the same round: query parts 8 apart,
-    // d halves 8 apart (or adjacent when nprob % 8 != 0)
-    const int mult = g.parts > 1 ? 8 * g.parts : DH ? (g.nprob % 8 == 0 ? 16 : 2) : 1;
+    // the query parts of one problem run in the same round, 8 apart
+    const int mult = g.parts > 1 ? 8 * g.parts : 1;
     const int grid = grid_for(kern, threads, g.nitems, mult);
     const float scale_log2 = 1.4426950408889634f / __builtin_sqrtf((float)D);
     hipLaunchKernelGGL(kfn, dim3(grid), dim3(threads), 0, st, g, static_cast<const uint16_t*>(q),
@@ -743,11 +760,10 @@ hipError_t launch_menu(const PassGeom& g0, const void* q, const void* k, const v
     if (tiles <= 16) return launch_one<D, 2, 8, 4, 2, 256, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
     if (tiles <= 24) return launch_one<D, 3, 8, 2, 2, 384, true, PAD, FAST>(g, 8, q, k, v, o, y, lse, st);
     // not split into query parts (in place, or a problem count not a multiple
-    // of 8): each problem becomes two items, one per half of d, 4 query tiles
-    // per wave (Q straight from memory: L = 512 does not fit an LDS stage)
-    g.dsplit = 1;
-    g.nitems = 2 * g.nprob;
-    return launch_one<D, 4, 8, 2, 2, 512, false, PAD, FAST, false, true>(g, 8, q, k, v, o, y, lse, st);
+    // of 8): whole problems, their query rows in two parts of 16 tiles on the
+    // 2-tile layout, the value rows kept in LDS from the first part (Q
+    // straight from memory: no LDS is left for a stage)
+    return launch_one<D, 2, 8, 4, 2, 512, false, PAD, FAST, false, true>(g, 8, q, k, v, o, y, lse, st);
 }
 
 template <int D, bool PAD>

@@ -300,9 +300,10 @@ def test_split_many_slots_global():
 def test_in_place_long_problems_against_oracle(fn):
     # lengths that split into query parts when not in place (m = 336 local,
     # N_w = 400 global, problem counts multiples of 8): in place a pass is
-    # never split by query rows; problems of 25-32 query tiles are split by
-    # halves of d instead (N_w = 400 and 500 global, m = 400 local; the halves
-    # of a problem 8 items apart, or adjacent for 6 problems), at d = 64 and 128
+    # never split across workgroups; a problem of 25-32 query tiles runs its
+    # two query parts one after the other with the value rows kept in LDS
+    # (N_w = 400 and 500 global, m = 400 local, 6 problems for N_w = 500), at
+    # d = 64 and 128
     import torch
     for geo, heads, d in (((21, 8, 8, 21, 4, 4), 8, 64), ((2, 20, 80, 1, 2, 4), 2, 64),
                           ((2, 20, 80, 1, 2, 4), 2, 128), ((2, 20, 75, 1, 2, 3), 1, 128),

@@ -68,8 +68,9 @@ def test_noalloc_float32_and_tiling_window():
 def test_noalloc_long_global_pass_in_place():
     # 2x20x79 padded to 2x20x80 with 1x2x4 windows: a 400-window global pass,
     # which the workspace entry point splits into query parts (Y in its
-    # workspace) and the no-allocation one runs in place as d-half items; both
-    # within the bar of the oracle and of each other
+    # workspace) and the no-allocation one runs in place, each problem's value
+    # rows kept in LDS across its two query parts; both within the bar of the
+    # oracle and of each other
     import torch
     for d in (64, 128):
         B, heads, grid, window = 1, 2, (2, 20, 79), (1, 2, 4)
