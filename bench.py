@@ -219,7 +219,6 @@ def summarize_profiles(prof_dir: str, workload: str, trace_log: str | None = Non
     # dk contributions (8 tensor-sizes); the local pass's reads q, k, v, dY and those contributions
     # and writes dq, dk, dv (9); per-row float32 arrays not counted
     for prefix, alg, what in (("squad_bwd_pass_bf16<128, false", 8 * tensor, "global pass"),
-                              ("squad_bwd_onesweep_global_bf16<128", 8 * tensor, "global pass, one sweep"),
                               ("squad_bwd_onesweep_bf16<128", 9 * tensor, "local pass, one sweep"),
                               ("squad_bwd_pass_bf16<128, true", 9 * tensor, "local pass")):
         kern = next((k for k in _kernels_with(rd, "TCC_EA0_RDREQ_sum") if k.startswith(prefix)), None)
