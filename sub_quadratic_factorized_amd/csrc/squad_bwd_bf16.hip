@@ -728,7 +728,8 @@ hipError_t launch_bwd_pass_bf16(const PassGeom& g, int d, const BwdArgs& a, hipS
     // the local pass (log-sum-exp and D given) of windows up to 12 key tiles:
     // the one-sweep kernel (32-bit row offsets within a batch element)
     if (a.lse && a.dd_in && !a.vdot && tiles <= 12 && g.n * g.heads * d < (int64_t(1) << 30)) {
-        if (tiles <= 8) return d == 128 ? launch_onesweep<128, 8, 4>(g, a, stream) : launch_onesweep<64, 8, 4>(g, a, stream);
+        if (tiles <= 8)
+            return d == 128 ? launch_onesweep<128, 8, 4>(g, a, stream) : launch_onesweep<64, 8, 4>(g, a, stream);
         return d == 128 ? launch_onesweep<128, 12, 1>(g, a, stream) : launch_onesweep<64, 12, 2>(g, a, stream);
     }
     if (a.lse) return d == 128 ? launch_d<128, true>(g, a, stream) : launch_d<64, true>(g, a, stream);

@@ -16,11 +16,12 @@
 //     parts one after the other, the first part keeping every value row in
 //     LDS for the second, so no value row is read from memory after the first
 //     part's outputs are written.
-//   * The work of an item is NB = ceil(L/32) steps (per query part).  Step b brings in 32 rows
-//     of K and of V (block b of this problem) and 32 rows of Q (block b of the
-//     NEXT item's query rows).  Every thread stages one 16-byte chunk of each in
-//     registers, PD steps ahead of use: ~PD * 3 * 32 * D * 2 bytes per
-//     workgroup are in flight while the MFMAs run.  Loads are unconditional
+//   * The work of an item (of each query part of it, above) is NB =
+//     ceil(L/32) steps.  Step b brings in 32 rows of K and of V (block b of
+//     this problem) and 32 rows of Q (block b of the NEXT item's query rows).
+//     Every thread stages one 16-byte chunk of each in registers, PD steps
+//     ahead of use: ~PD * 3 * 32 * D * 2 bytes per workgroup are in flight
+//     while the MFMAs run.  Loads are unconditional
 //     (rows past the end clamped to the last row; steps past the last item
 //     read one fixed chunk, or, through buffer descriptors, nothing), so each
 //     stays in flight until its data is stored.
