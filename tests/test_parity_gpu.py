@@ -271,7 +271,8 @@ def test_many_heads_small_dim(dtype, op):
 
 # ---------------------------------------------------------------------------
 # Long problems: whole on the 2- and 3-tile instances up to 24 tiles, split
-# into query parts beyond (problem count a multiple of 8, not in place)
+# into query parts beyond (problem count a multiple of 8, not in place), else
+# whole with their two query parts in turn and the value rows kept in LDS
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("geo,heads", [
@@ -288,6 +289,17 @@ def test_split_long_problems(geo, heads, op):
 def test_split_long_problems_head_dim_64():
     run_small((21, 8, 8, 21, 4, 4), "bf16", "local", heads=8, d=64, seed=18)   # whole, 3 tiles per wave
     run_small((5, 16, 10, 5, 8, 10), "bf16", "local", heads=4, d=64, seed=18)  # 2 parts
+
+
+@pytest.mark.parametrize("geo,heads,op,d", [
+    ((5, 16, 10, 5, 8, 10), 3, "local", 128),   # m = 400, 6 problems: resident values, buffer loader
+    ((5, 16, 10, 5, 8, 10), 3, "fwd", 128),
+    ((5, 16, 10, 5, 8, 10), 3, "local", 64),
+    ((2, 20, 75, 1, 2, 3), 1, "global", 128),   # N_w = 500 (32 tiles), 6 problems, out of place
+    ((2, 20, 75, 1, 2, 3), 1, "global", 64),
+])
+def test_long_problems_not_split_out_of_place(geo, heads, op, d):
+    run_small(geo, "bf16", op, heads=heads, d=d, seed=21)
 
 
 def test_split_many_slots_global():
@@ -307,7 +319,7 @@ def test_in_place_long_problems_against_oracle(fn):
     import torch
     for geo, heads, d in (((21, 8, 8, 21, 4, 4), 8, 64), ((2, 20, 80, 1, 2, 4), 2, 64),
                           ((2, 20, 80, 1, 2, 4), 2, 128), ((2, 20, 75, 1, 2, 3), 1, 128),
-                          ((1, 20, 40, 1, 20, 20), 2, 128)):
+                          ((1, 20, 40, 1, 20, 20), 2, 128), ((1, 20, 40, 1, 20, 20), 2, 64)):
         T, Hs, Ws, wt, wh, ww = geo
         log(f"case in-place {fn} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} heads={heads}")
         q, k, v = wl.random_geometry_inputs(1, heads, T * Hs * Ws, d, "bf16", seed=23)
