@@ -25,7 +25,8 @@ void check_v() {
     using G = BlockGeo<D>;
     const int size = kBlockRows * G::VSTR;
     std::vector<long> v(size, -1);
-    // stores: chunk ch = (row, 16-byte column), halves swapped in registers
+    // stores: chunk ch = (row, 16-byte column); on swapped row groups its two
+    // 8-byte halves trade places (the kernels store each half at its own address)
     for (int ch = 0; ch < G::NCH; ++ch) {
         const int r = ch / G::KC, c = ch % G::KC;
         const int base = v_chunk_offset<D>(r, c);
