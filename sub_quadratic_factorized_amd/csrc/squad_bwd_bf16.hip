@@ -205,6 +205,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
     bf16x8 qreg[G::KS], doreg[G::KS];
     float Dq = 0.0f, m = -INFINITY, lpart = 0.0f, lse2 = 0.0f;
     f32x4 dqacc[G::DT];
+    // With one group of key tiles, the key tile of sweep B is this wave's own
+    // (tile `wave`), and its K and V rows pass through LDS in sweep A's step
+    // wave / 2: they are kept in registers from there instead of being read
+    // from memory again at the start of sweep B (8-wave instances: the
+    // 12-wave ones have no registers to spare).
+    const bool kv_early = NW <= 8 && ngroups == 1;
+    bf16x8 kreg[G::KS], vreg[G::KS];
     int st = 0;  // step of sweep A
     for (int s0 = 0; s0 < nsteps_a; s0 += PD) {
 #pragma unroll
@@ -244,6 +251,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
                 for (int dt = 0; dt < G::DT; ++dt) dqacc[dt] = zero;
             }
             __syncthreads();
+            if (kv_early && st < live_a && blk == (wave >> 1) && wave < ntiles) {
+#pragma unroll
+                for (int s = 0; s < G::KS; ++s) {
+                    kreg[s] = row_op(rowA[u & 1], wave & 1, s);
+                    vreg[s] = row_op(rowB[u & 1], wave & 1, s);
+                }
+            }
             if (!active) continue;
             // dQ^T += K^T dS^T
             f32x4 sa = zero, sb = zero, pa = zero, pb = zero;
@@ -307,7 +321,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
 
     // ---- sweep B: per key group, dV and dK over Q and dO --------------------
     // (every row's log-sum-exp and D reached LDS before the barriers since)
-    bf16x8 kreg[G::KS], vreg[G::KS];
     f32x4 dkacc[G::DT], dvacc[G::DT];
     st = 0;  // step of sweep B
     for (int s0 = nsteps_a; s0 < nsteps; s0 += PD) {
@@ -320,8 +333,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW > 8 
             put(sx1[u], sx2[u], u & 1, kDkv);
             issue(sx1[u], sx2[u]);
             if (active && qb == 0) {
-                load_tile(kp, kt, kreg);
-                load_tile(vp, kt, vreg);
+                if (!kv_early) {
+                    load_tile(kp, kt, kreg);
+                    load_tile(vp, kt, vreg);
+                }
 #pragma unroll
                 for (int dt = 0; dt < G::DT; ++dt) dkacc[dt] = dvacc[dt] = zero;
             }
