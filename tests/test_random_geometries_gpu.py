@@ -1,9 +1,10 @@
 """GPU parity on seeded random geometries: batch, heads, head dimension, grid
 and window drawn from a fixed generator (the list is the same on every run),
 with window lengths and window counts spread over 1..512, so that the launch
-menu's instances meet the batch and head strides, ragged last blocks and
+menus' instances meet the batch and head strides, ragged last blocks and
 problem counts in combinations no hand-written case names.  The whole output
-of squad_attn_fwd is compared with the fp64 oracle at the bar of its dtype."""
+of squad_attn_fwd, and the three gradients of squad_attn_bwd, are compared
+with the fp64 oracle at the bars of their dtype."""
 
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ from oracle import squad_oracle as so
 from sub_quadratic_factorized_amd import binding as bd
 from sub_quadratic_factorized_amd import workloads as wl
 
-from gpu_common import assert_close, host_to_device, log, to_f64
+from gpu_common import assert_close, errors, host_to_device, log, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +25,7 @@ def _bucket(L):
     return 0 if t <= 12 else 1 if t <= 16 else 2 if t <= 24 else 3
 
 
-def _cases(per_bucket=10, seed=2024):
+def _cases(per_bucket=10, seed=2024, max_tokens=MAX_TOKENS):
     # ten cases for each range of the longer pass's query tiles (<= 12, 13-16,
     # 17-24, 25-32), drawn in order from one seeded stream
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -33,7 +34,7 @@ def _cases(per_bucket=10, seed=2024):
         wt, wh, ww = (int(x) for x in rng.integers(1, 17, size=3))
         ct, cy, cx = (int(x) for x in rng.integers(1, 17, size=3))
         m, nw = wt * wh * ww, ct * cy * cx
-        if m > 512 or nw > 512 or m * nw > MAX_TOKENS:
+        if m > 512 or nw > 512 or m * nw > max_tokens:
             continue
         b = _bucket(max(m, nw))
         if len(buckets[b]) >= per_bucket:
@@ -47,6 +48,10 @@ def _cases(per_bucket=10, seed=2024):
 
 
 CASES = _cases()
+# the gradients: four cases per range, smaller grids (the oracle's backward
+# costs about five forwards)
+BWD_CASES = _cases(per_bucket=4, seed=4048, max_tokens=4000)
+GRAD_BAR = {"bf16": 1e-2, "f32": 1e-5}  # relative L2 per gradient, as the backward tests
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -73,3 +78,29 @@ def test_random_geometry(case):
     torch.cuda.synchronize()
     ref = so.squad_attention(q, k, v, (B, heads, T, Hs, Ws, wt, wh, ww, d))
     assert_close(to_f64(out), ref, dtype, "fwd")
+
+
+@pytest.mark.parametrize("case", BWD_CASES,
+                         ids=[f"B{c[0]}h{c[1]}d{c[2]}{c[3]}_{'x'.join(map(str, c[4]))}_w{'x'.join(map(str, c[5]))}"
+                              for c in BWD_CASES])
+def test_random_geometry_backward(case):
+    import torch
+    B, heads, d, dtype, grid, window = case
+    T, Hs, Ws = grid
+    wt, wh, ww = window
+    n = T * Hs * Ws
+    log(f"case bwd B={B} heads={heads} d={d} {dtype} grid={T}x{Hs}x{Ws} window={wt}x{wh}x{ww} "
+        f"m={wt * wh * ww} N_w={n // (wt * wh * ww)}")
+    q, k, v = wl.random_geometry_inputs(B, heads, n, d, dtype, seed=9)
+    do = wl.random_geometry_inputs(B, heads, n, d, dtype, seed=1009)[0]
+    qd, kd, vd, dod = host_to_device((q, k, v, do), dtype)
+    out = bd.squad_attn_fwd(qd, kd, vd, grid, window)
+    grads = bd.squad_attn_bwd(qd, kd, vd, out, dod, grid, window)
+    torch.cuda.synchronize()
+    ref = so.squad_backward(q, k, v, do, (B, heads, T, Hs, Ws, wt, wh, ww, d))
+    worst = 0.0
+    for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+        max_abs, rel = errors(to_f64(g), r)
+        log(f"  {name}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+        worst = max(worst, rel)
+    assert worst <= GRAD_BAR[dtype], (case, worst)
